@@ -1,0 +1,226 @@
+"""Benchmark of the tiled-VAE decode-assembly hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * blend + crop + stitch of the 49-frame 480x832 bf16 video decode: 75 tiles
+    (5 temporal x 3 x 5 spatial; 17-frame / 256x256 tiles, strides 12 / 192,
+    blend 5 / 64) into [1,3,49,480,832] -- row, column and frame seams;
+  * patch GroupNorm of the bf16 decoder activation [1,128,13,60,104], 32
+    groups, 4 patches along H, eps 1e-6, affine.
+Inputs are resident in HBM before timing.  Throughput is algorithmic bytes per
+second: blend = (all tile elements + all output elements) x 2 B, GroupNorm =
+3 x |x| x 2 B (two reads and one write of the two-pass method).
+
+Prints one JSON line (rank 0, N=1 only).  The oracle (plain C, all host cores)
+is timed on the same workload as the CPU baseline, and its output is compared
+with the GPU's (bit-exact blend, GroupNorm within tolerance).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD specification
+METRIC = "tiled-VAE blend+stitch and patch-GroupNorm HBM GB/s (% of peak), 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=4, help="workload (the default is the one reported)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flushed-reps", type=int, default=30,
+                    help="extra per-part timings with a 512 MB cache flush before each (0 = skip)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import seam_blending_patch_amd as sb
+    import workloads
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workloads.CONFIGS[args.config]
+    bw, tiles = workloads.draw_config_blend(args.config)
+    has_gn = cfg.groupnorm is not None
+    if has_gn:
+        gw, (x_np, g_np, b_np) = workloads.draw_config_groupnorm(args.config)
+
+    def dev_t(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    nt, nh, nw = bw.grid
+    flat = [dev_t(t, bw.dtype).reshape(bw.tile_shape(k // (nh * nw), (k // nw) % nh, k % nw))
+            for k, t in enumerate(tiles)]
+    grid = [[[flat[(tau * nh + i) * nw + j] for j in range(nw)] for i in range(nh)] for tau in range(nt)]
+    grid_arg = grid[0] if bw.ndim == 4 else grid
+    out = sb.vae_tile_blend_stitch(grid_arg, bw.blend, bw.row_limit)
+    blend_bytes = (bw.tile_elems() + out.numel()) * out.element_size()
+    if has_gn:
+        x = dev_t(x_np, gw.dtype)
+        g = dev_t(g_np, gw.dtype)
+        b = dev_t(b_np, gw.dtype)
+        y = torch.empty_like(x)
+        ws = torch.empty(sb.patch_groupnorm_workspace_bytes(tuple(x.shape), gw.groups, gw.split_axis,
+                                                            gw.n_patches), dtype=torch.uint8, device=dev)
+        gn_bytes = 3 * x.numel() * x.element_size()
+    else:
+        gn_bytes = 0
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sb.vae_tile_blend_stitch(grid_arg, bw.blend, bw.row_limit, out=out)
+        if ev is not None:
+            ev[1].record()
+        if has_gn:
+            sb.patch_groupnorm(x, gw.groups, gw.split_axis, gw.n_patches, gw.eps, g, b, out=y,
+                               workspace=ws)
+            if ev is not None:
+                ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    blend_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    gn_ms = [e[1].elapsed_time(e[2]) for e in evs] if has_gn else [0.0]
+    blend_avg_us = 1e3 * sum(blend_ms) / len(blend_ms)
+    gn_avg_us = 1e3 * sum(gn_ms) / len(gn_ms)
+    total_bytes = blend_bytes + gn_bytes
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    blend_gbs = blend_bytes / (blend_avg_us * 1e-6) / 1e9
+    gn_gbs = gn_bytes / (gn_avg_us * 1e-6) / 1e9 if has_gn else None
+    print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; blend {blend_avg_us:.1f} us "
+          f"({blend_gbs:.0f} GB/s), groupnorm {gn_avg_us:.1f} us", file=sys.stderr, flush=True)
+
+    # optional: the same parts with the 256 MB last-level cache flushed first
+    flushed = None
+    if args.flushed_reps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fb, fg = [], []
+        for _ in range(args.flushed_reps):
+            scratch.fill_(1)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            step(e)
+            torch.cuda.synchronize()
+            fb.append(e[0].elapsed_time(e[1]))
+            if has_gn:
+                fg.append(e[1].elapsed_time(e[2]))
+        del scratch
+        med_b = float(np.median(fb)) * 1e3
+        flushed = {"blend_us_median": med_b, "blend_GBps": blend_bytes / (med_b * 1e-6) / 1e9}
+        if has_gn:
+            med_g = float(np.median(fg)) * 1e3
+            flushed.update({"groupnorm_us_median": med_g, "groupnorm_GBps": gn_bytes / (med_g * 1e-6) / 1e9})
+
+    # traffic from committed PMC counters, only while the kernel source is unchanged
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "blend_traffic.json")
+    src = os.path.join(ROOT, "seam_blending_patch_amd", "csrc", "blend_stitch.hip")
+    if os.path.exists(tpath):
+        rec = json.load(open(tpath))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("kernel_sha256") == sha and rec.get("config") == args.config:
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    # parity of this run's output and the CPU baseline (the oracle on all host cores)
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    cpu = None
+    parity = {}
+    if not args.no_cpu_baseline:
+        tc0 = time.perf_counter()
+        want = oracle.blend_workload(bw, tiles)
+        tc1 = time.perf_counter()
+        got = out.cpu()
+        got = got.view(torch.int16).numpy().view(np.uint16) if bw.dtype == "bf16" else got.numpy()
+        isz = {"fp32": np.uint32, "fp16": np.uint16, "bf16": np.uint16}[bw.dtype]
+        parity["blend_mismatches"] = int(np.sum(got.view(isz) != want.view(isz)))
+        cpu_s = tc1 - tc0
+        if has_gn:
+            tc2 = time.perf_counter()
+            ref, _, _ = oracle.groupnorm(x_np, gw.groups, gw.eps, g_np, b_np, gw.dtype)
+            tc3 = time.perf_counter()
+            cpu_s += tc3 - tc2
+            yv = y.cpu()
+            yv = ((yv.view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+                  if gw.dtype == "bf16" else yv.float().numpy())
+            d = np.abs(yv.astype(np.float64) - ref)
+            tol = (np.maximum(1e-2, np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0**-126))) - 7))
+                   if gw.dtype == "bf16" else
+                   np.maximum(1e-2, np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0**-14))) - 10))
+                   if gw.dtype == "fp16" else 1e-5 * np.maximum(1.0, np.abs(ref)))
+            parity["groupnorm_out_of_tol"] = int(np.sum(d > tol))
+            parity["groupnorm_max_abs_err"] = float(d.max())
+        cpu = {"value": total_bytes / cpu_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"one full step of the same workload (blend+stitch {bw.name} and "
+                         f"{gw.name if has_gn else 'no GroupNorm'}), {cpu_s:.2f} s on {threads} threads",
+               "seconds": cpu_s}
+
+    wl = {4: "video 5-D bf16 decode assembly: 75 tiles (5 temporal x 3 x 5; 17-frame 256x256, "
+             "strides 12/192/192, blend 5/64/64) -> [1,3,49,480,832], plus patch GroupNorm "
+             "[1,128,13,60,104] G=32, 4 patches along H"}.get(args.config, cfg.title)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": bw.dtype,
+        "data": "synthetic (seeded; N(0,0.5) clamped tiles, N(0,1)+per-patch offset activations)",
+        "config": {"workload": wl, "config_index": args.config, "blend_bytes": blend_bytes,
+                   "groupnorm_bytes": gn_bytes, "parallelism": "single GPU"},
+        "frac_of_peak": value / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "achieved": blend_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": blend_gbs / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "blend_stitch_kernel", "launch_us": blend_avg_us},
+        "parts": {"blend": {"bytes": blend_bytes, "us": blend_avg_us, "GBps": blend_gbs},
+                  "groupnorm": {"bytes": gn_bytes, "us": gn_avg_us, "GBps": gn_gbs}},
+        "flushed": flushed,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

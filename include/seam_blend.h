@@ -1,0 +1,146 @@
+/*
+ * seam_blend.h -- C ABI of the MI355X (gfx950) tiled-VAE decode-assembly library.
+ *
+ * Two operations, each behind one entry point:
+ *
+ *  vae_tile_blend_stitch  -- crossfade overlapping decoded tiles along rows
+ *      (blend_v), columns (blend_h) and frames (blend_t), crop every tile to the
+ *      row limit and stitch the result into one output, written once.
+ *      Defined by: diffusers issue "[Proposal] Vectorize tiled VAE blending
+ *      while preserving rounding and CUDA graph replay", section "Proposed
+ *      scope" (blend_v / blend_h / blend_t; extent clamping from diffusers
+ *      #2660; in-place output; per-product rounding; coefficients from float64
+ *      division).
+ *
+ *  patch_groupnorm -- GroupNorm of a tensor viewed as spatial patches: per-patch
+ *      (count, mean, M2) statistics merged with Chan's formula so that the
+ *      result equals unsplit GroupNorm (global mean, variance divided by the
+ *      count).  Defined by: DistVAE PR "Add tiled VAE parallelism & extended
+ *      model support", the PatchGroupNorm commits and the Patchify commit
+ *      (first patches one band longer).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named "device" are HIP device pointers (any device memory the
+ *    current device can read/write); everything else is host memory read
+ *    during the call only.  The caller owns and allocates every buffer.  The
+ *    library allocates no device memory, never synchronises the stream and
+ *    keeps no state other than a thread-local error message.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream),
+ *    on the device that is current when the call is made.  Results are ready
+ *    when the stream reaches that point.
+ *  - Return value: 0 on success, or a negative SB_E* code; the message is then
+ *    available from seamblend_last_error().  Argument and geometry errors are
+ *    detected on the host before anything is enqueued.  Faults during
+ *    execution surface asynchronously on the stream, as for any HIP kernel.
+ *  - Tensors are dense, contiguous, row-major (last index fastest).
+ */
+#ifndef SEAM_BLEND_H
+#define SEAM_BLEND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage dtype of every tile / tensor in one call */
+typedef enum { SB_F32 = 0, SB_F16 = 1, SB_BF16 = 2 } sb_dtype;
+
+/* return codes */
+#define SB_OK 0
+#define SB_EARG (-1)       /* bad argument: null pointer, unknown dtype, bad rank ... */
+#define SB_EGEOM (-2)      /* geometry outside what the data-parallel kernel supports */
+#define SB_EWORKSPACE (-3) /* workspace smaller than patch_groupnorm_workspace_bytes() */
+#define SB_ELAUNCH (-4)    /* the HIP runtime rejected a launch (message from hipGetErrorString) */
+
+/*
+ * Output extents of vae_tile_blend_stitch for a tile grid, after the same
+ * validation the entry point performs (host only, no device work).
+ *   grid[6]        {ndim (4 or 5), N, C, n_t, n_h, n_w}; n_t must be 1 when ndim == 4.
+ *   tile_extents   n_t + n_h + n_w entries: t_0..t_{n_t-1}, h_0.., w_0..
+ *                  (t_0 must be 1 when ndim == 4).
+ *   blend_extent   {E_t, E_h, E_w} >= 0; E_t is ignored when ndim == 4.
+ *   row_limit      {R_t, R_h, R_w} >= 1: stride between tile origins along
+ *                  each axis, and the crop of every tile but the last.
+ *   out_extents    receives {L_t, L_h, L_w}, L = (n - 1) * R + (last extent).
+ * Geometry preconditions (else SB_EGEOM): every non-last tile is >= R long;
+ * with e(k) = min(E, ext(k-1), ext(k)) the blend extent between tiles k-1 and
+ * k (e(0) = 0), every tile satisfies ext(k) >= e(k) + e(k+1), so a tile's head
+ * seam and tail never overlap; at most 64 tiles per axis; output planes and
+ * tiles below 2^31 elements per (n, c) plane.
+ */
+int vae_tile_blend_stitch_output_extents(const int64_t grid[6], const int64_t *tile_extents,
+                                         const int64_t blend_extent[3],
+                                         const int64_t row_limit[3], int64_t out_extents[3]);
+
+/*
+ * Blend + crop + stitch of a tile grid into `out`.
+ *   tiles        host array of n_t*n_h*n_w device pointers in raster order
+ *                (tau, i, j): tile (tau, i, j) is a contiguous
+ *                [N, C, t_tau, h_i, w_j] array (ndim 5) or [N, C, h_i, w_j]
+ *                (ndim 4) of `dtype`.  Tiles are only read.
+ *   grid, tile_extents, blend_extent, row_limit: as above.
+ *   dtype        SB_F32, SB_F16 or SB_BF16 (tiles and output alike).
+ *   out          device pointer to a contiguous [N, C, L_t, L_h, L_w] (ndim 5)
+ *                or [N, C, L_h, L_w] (ndim 4) array of `dtype`; must not
+ *                overlap any tile (checked, SB_EARG).
+ *   stream       hipStream_t or NULL.
+ * Result: for each temporal tile, tiles are blended in raster order, row seam
+ * (with the tile above, as already blended) before column seam (with the tile
+ * to the left, as already blended), each seam element
+ *   RN_T( RN_T(a * w_a[k]) + RN_T(b * w_b[k]) ),  w_b[k] = fp32(k/e),
+ *   w_a[k] = fp32(1 - k/e) from double, products and sum in fp32 without
+ *   fusion;
+ * every tile is cropped to R except the last along each axis; then each
+ * stitched temporal chunk is blended with the previous stitched chunk (as
+ * already blended) along frames and cropped.  Bit-exact for every dtype.
+ * Each output element is written exactly once; no scratch memory.
+ */
+int vae_tile_blend_stitch(const void *const *tiles, const int64_t grid[6],
+                          const int64_t *tile_extents, const int64_t blend_extent[3],
+                          const int64_t row_limit[3], int dtype, void *out, void *stream);
+
+/*
+ * Device workspace (bytes) patch_groupnorm needs for this problem; 0 with an
+ * error message for invalid arguments.  shape: ndim entries {N, C, spatial..}.
+ */
+size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape, int64_t groups,
+                                       int split_axis, int64_t n_patches);
+
+/*
+ * GroupNorm of x viewed as n_patches patches along split_axis.
+ *   x            device pointer, contiguous [N, C, spatial...] of dtype, ndim 3..5.
+ *   shape        host array of ndim extents; C % groups == 0.
+ *   split_axis   2 <= split_axis < ndim: the spatial axis the patches cut.
+ *   n_patches    1..64.  Patch p covers [s_p, s_p + len_p) along split_axis
+ *                with the first (L mod P) patches one longer (empty patches
+ *                allowed when P > L).
+ *   eps          added to the variance (fp32), >= 0.
+ *   gamma, beta  device pointers to [C] of dtype, or NULL (1 and 0).
+ *   out          device pointer like x; may be x itself (in place).
+ *   workspace    device scratch of at least patch_groupnorm_workspace_bytes();
+ *                caller-owned, contents need not be initialised.
+ *   patch_stats  optional device pointer to N*G*P*3 floats, or NULL: receives
+ *                per-patch (count, mean, M2), M2 = sum of squared deviations
+ *                about the patch mean, merged in fp32 over that patch's chunks.
+ *   stream       hipStream_t or NULL.
+ * Result: per (n, g), mean and M2 over the C/G channels and all spatial
+ * positions, obtained by Chan-merging fp32 partial statistics in a fixed order
+ * (chunks of a patch, then patches); var = M2 / count; rstd = 1/sqrt(var+eps);
+ * y = (x - mean) * rstd * gamma_c + beta_c in fp32, rounded once to dtype.
+ * Deterministic: the same inputs give the same bits on every call.
+ */
+int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t groups,
+                    int split_axis, int64_t n_patches, float eps, const void *gamma,
+                    const void *beta, int dtype, void *out, void *workspace,
+                    size_t workspace_bytes, float *patch_stats, void *stream);
+
+/* Thread-local message describing the last non-zero return on this thread. */
+const char *seamblend_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEAM_BLEND_H */

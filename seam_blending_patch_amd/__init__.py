@@ -1,0 +1,223 @@
+"""MI355X (gfx950) tiled-VAE decode assembly: blend + crop + stitch of
+overlapping decoded tiles, and patch-split GroupNorm.
+
+This module is the thin Python binding of ``libseamblend.so`` (C ABI in
+``include/seam_blend.h``): it turns torch tensors into pointers, sizes and the
+current HIP stream and calls the library.  PyTorch is used for device memory
+and streams only; every step of both operations runs in the library's HIP
+kernels.  There is no CPU fallback: importing this package fails if the
+library has not been built, and every call requires GPU tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+__all__ = ["vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents",
+           "patch_groupnorm", "patch_groupnorm_workspace_bytes", "SeamBlendError", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseamblend.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
+                      "g.build()' or python seam_blending_patch_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_lib.vae_tile_blend_stitch_output_extents.argtypes = [_i64p, _i64p, _i64p, _i64p, _i64p]
+_lib.vae_tile_blend_stitch_output_extents.restype = ctypes.c_int
+_lib.vae_tile_blend_stitch.argtypes = [ctypes.POINTER(ctypes.c_void_p), _i64p, _i64p, _i64p, _i64p,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+_lib.vae_tile_blend_stitch.restype = ctypes.c_int
+_lib.patch_groupnorm_workspace_bytes.argtypes = [ctypes.c_int, _i64p, ctypes.c_int64, ctypes.c_int,
+                                                 ctypes.c_int64]
+_lib.patch_groupnorm_workspace_bytes.restype = ctypes.c_size_t
+_lib.patch_groupnorm.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64p, ctypes.c_int64, ctypes.c_int,
+                                 ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+_lib.patch_groupnorm.restype = ctypes.c_int
+_lib.seamblend_last_error.argtypes = []
+_lib.seamblend_last_error.restype = ctypes.c_char_p
+
+_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class SeamBlendError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _lib.seamblend_last_error().decode(errors="replace")
+        super().__init__(f"{where} failed ({code}): {msg}")
+        self.code = code
+
+
+def _arr(vals: Sequence[int]):
+    return (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise SeamBlendError(rc, where)
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_gpu(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in _DTYPE:
+        raise TypeError(f"{name}: unsupported dtype {t.dtype}")
+
+
+def _triple(v, name):
+    if isinstance(v, int):
+        return (v, v, v)
+    v = tuple(int(a) for a in v)
+    if len(v) == 2:
+        return (0,) + v
+    if len(v) != 3:
+        raise ValueError(f"{name} must be an int, (h, w) or (t, h, w)")
+    return v
+
+
+def _grid_of(tiles):
+    """Nested tiles -> (ndim, flat list in raster order, n_t, n_h, n_w)."""
+    first = tiles[0][0]
+    if isinstance(first, torch.Tensor):  # [i][j] of 4-D tiles
+        grid3 = [tiles]
+    else:
+        grid3 = tiles
+    flat = [t for plane in grid3 for row in plane for t in row]
+    nt, nh, nw = len(grid3), len(grid3[0]), len(grid3[0][0])
+    for plane in grid3:
+        if len(plane) != nh or any(len(r) != nw for r in plane):
+            raise ValueError("tile grid is ragged")
+    ndim = flat[0].dim()
+    if ndim not in (4, 5) or (ndim == 4 and nt != 1) or any(t.dim() != ndim for t in flat):
+        raise ValueError("tiles must be 4-D [N,C,h,w] in an [i][j] grid or 5-D [N,C,t,h,w] in [tau][i][j]")
+    return ndim, grid3, flat, nt, nh, nw
+
+
+def _extents(grid3, ndim, nt, nh, nw):
+    t0 = grid3[0][0][0]
+    N, C = t0.shape[0], t0.shape[1]
+    et = [grid3[tau][0][0].shape[2] if ndim == 5 else 1 for tau in range(nt)]
+    eh = [grid3[0][i][0].shape[-2] for i in range(nh)]
+    ew = [grid3[0][0][j].shape[-1] for j in range(nw)]
+    for tau in range(nt):
+        for i in range(nh):
+            for j in range(nw):
+                t = grid3[tau][i][j]
+                want = (N, C, et[tau], eh[i], ew[j]) if ndim == 5 else (N, C, eh[i], ew[j])
+                if tuple(t.shape) != want:
+                    raise ValueError(f"tile ({tau},{i},{j}) has shape {tuple(t.shape)}, expected {want}")
+    return N, C, et, eh, ew
+
+
+def vae_tile_blend_stitch_output_extents(grid: Sequence[int], tile_extents: Sequence[int],
+                                         blend_extent: Sequence[int], row_limit: Sequence[int]):
+    """(L_t, L_h, L_w) of the stitched output (host-only validation)."""
+    out = (ctypes.c_int64 * 3)()
+    _check(_lib.vae_tile_blend_stitch_output_extents(_arr(grid), _arr(tile_extents),
+                                                     _arr(blend_extent), _arr(row_limit), out),
+           "vae_tile_blend_stitch_output_extents")
+    return tuple(out)
+
+
+def vae_tile_blend_stitch(tiles, blend_extent: Union[int, Sequence[int]],
+                          row_limit: Union[int, Sequence[int]],
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Blend, crop and stitch a grid of decoded tiles on the GPU.
+
+    tiles: ``tiles[i][j]`` 4-D ``[N,C,h_i,w_j]`` or ``tiles[tau][i][j]`` 5-D
+    ``[N,C,t_tau,h_i,w_j]`` contiguous GPU tensors of one dtype (fp32, fp16,
+    bf16).  blend_extent / row_limit: int, (h, w) or (t, h, w).
+    Returns (or fills) the ``[N,C,(L_t,)L_h,L_w]`` output.
+    """
+    ndim, grid3, flat, nt, nh, nw = _grid_of(tiles)
+    for k, t in enumerate(flat):
+        _require_gpu(t, f"tile {k}")
+    dtype, device = flat[0].dtype, flat[0].device
+    if any(t.dtype != dtype or t.device != device for t in flat):
+        raise ValueError("all tiles must share dtype and device")
+    N, C, et, eh, ew = _extents(grid3, ndim, nt, nh, nw)
+    E, R = _triple(blend_extent, "blend_extent"), _triple(row_limit, "row_limit")
+    if ndim == 4:
+        E, R = (0, E[1], E[2]), (1, R[1], R[2])
+    grid = (ndim, N, C, nt, nh, nw)
+    ext = list(et) + list(eh) + list(ew)
+    LT, LH, LW = vae_tile_blend_stitch_output_extents(grid, ext, E, R)
+    shape = (N, C, LH, LW) if ndim == 4 else (N, C, LT, LH, LW)
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=device)
+    else:
+        _require_gpu(out, "out")
+        if tuple(out.shape) != shape or out.dtype != dtype or out.device != device:
+            raise ValueError(f"out must be {shape} {dtype} on {device}")
+    ptrs = (ctypes.c_void_p * len(flat))(*[t.data_ptr() for t in flat])
+    with torch.cuda.device(device):
+        rc = _lib.vae_tile_blend_stitch(ptrs, _arr(grid), _arr(ext), _arr(E), _arr(R), _DTYPE[dtype],
+                                        ctypes.c_void_p(out.data_ptr()),
+                                        ctypes.c_void_p(_stream_ptr(device)))
+    _check(rc, "vae_tile_blend_stitch")
+    return out
+
+
+def patch_groupnorm_workspace_bytes(shape: Sequence[int], groups: int, split_axis: int,
+                                    n_patches: int) -> int:
+    n = _lib.patch_groupnorm_workspace_bytes(len(shape), _arr(shape), groups, split_axis, n_patches)
+    if n == 0:
+        raise SeamBlendError(-1, "patch_groupnorm_workspace_bytes")
+    return int(n)
+
+
+def patch_groupnorm(x: torch.Tensor, groups: int, split_axis: int, n_patches: int,
+                    eps: float = 1e-6, gamma: Optional[torch.Tensor] = None,
+                    beta: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    patch_stats: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GroupNorm of x ([N,C,...] GPU tensor) from per-patch statistics merged
+    with Chan's formula; equals unsplit GroupNorm.  ``out`` may be ``x``.
+    ``workspace``: optional uint8 GPU tensor of at least
+    ``patch_groupnorm_workspace_bytes`` bytes (allocated here if omitted).
+    ``patch_stats``: optional float32 GPU tensor [N, G, P, 3] that receives
+    per-patch (count, mean, M2)."""
+    _require_gpu(x, "x")
+    shape = tuple(x.shape)
+    dev = x.device
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _require_gpu(t, name)
+            if t.dtype != x.dtype or t.numel() != shape[1] or t.device != dev:
+                raise ValueError(f"{name} must be [C] of x's dtype on x's device")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _require_gpu(out, "out")
+        if tuple(out.shape) != shape or out.dtype != x.dtype or out.device != dev:
+            raise ValueError("out must match x")
+    need = patch_groupnorm_workspace_bytes(shape, groups, split_axis, n_patches)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.device != dev:
+        raise ValueError("workspace must be a GPU tensor on x's device")
+    if patch_stats is not None:
+        if (patch_stats.dtype != torch.float32 or not patch_stats.is_cuda or not patch_stats.is_contiguous()
+                or patch_stats.numel() != shape[0] * groups * n_patches * 3):
+            raise ValueError("patch_stats must be a contiguous float32 GPU tensor [N, G, P, 3]")
+    with torch.cuda.device(dev):
+        rc = _lib.patch_groupnorm(
+            ctypes.c_void_p(x.data_ptr()), x.dim(), _arr(shape), groups, split_axis, n_patches,
+            float(eps), ctypes.c_void_p(gamma.data_ptr() if gamma is not None else None),
+            ctypes.c_void_p(beta.data_ptr() if beta is not None else None), _DTYPE[x.dtype],
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+            workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(patch_stats.data_ptr() if patch_stats is not None else None),
+            ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "patch_groupnorm")
+    return out

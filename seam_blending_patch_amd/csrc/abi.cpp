@@ -1,0 +1,402 @@
+// abi.cpp -- host side of the C ABI declared in include/seam_blend.h:
+// argument and geometry validation, the per-axis geometry of the tile grid
+// (clamped blend extents, crops, origins), the distinct-extent coefficient
+// table layout, launch windows, GroupNorm patch/chunk layout and workspace.
+// No device memory is allocated and the stream is never synchronised.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/seam_blend.h"
+#include "sb_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int elem_bytes(int dtype) { return dtype == SB_F32 ? 4 : 2; }
+
+// --------------------------------------------------------------------------
+// tile-grid geometry
+// --------------------------------------------------------------------------
+struct Axis {
+  int64_t n = 0, E = 0, R = 0, L = 0;
+  std::vector<int64_t> ext, e; // e[k]: clamped blend extent between k-1 and k (e[0] = 0)
+};
+
+struct Grid {
+  int ndim = 0;
+  int64_t N = 0, C = 0;
+  Axis ax[3]; // t, h, w
+};
+
+int build_grid(const int64_t grid[6], const int64_t *tile_extents, const int64_t blend_extent[3],
+               const int64_t row_limit[3], Grid &G) {
+  if (!grid || !tile_extents || !blend_extent || !row_limit)
+    return fail(SB_EARG, "null geometry pointer");
+  G.ndim = (int)grid[0];
+  if (G.ndim != 4 && G.ndim != 5) return fail(SB_EARG, "ndim must be 4 or 5 (got %lld)", (long long)grid[0]);
+  G.N = grid[1];
+  G.C = grid[2];
+  if (G.N < 0 || G.C < 0) return fail(SB_EARG, "N and C must be >= 0");
+  const char *names[3] = {"t", "h", "w"};
+  int64_t off = 0;
+  for (int a = 0; a < 3; ++a) {
+    Axis &A = G.ax[a];
+    A.n = grid[3 + a];
+    if (A.n < 1) return fail(SB_EARG, "grid count along %s must be >= 1", names[a]);
+    if (A.n > sb::kMaxAxisTiles)
+      return fail(SB_EGEOM, "at most %d tiles per axis (got %lld along %s)", sb::kMaxAxisTiles,
+                  (long long)A.n, names[a]);
+    A.E = blend_extent[a];
+    A.R = row_limit[a];
+    if (G.ndim == 4 && a == 0) {
+      A.E = 0;
+      A.R = 1;
+      if (A.n != 1) return fail(SB_EARG, "n_t must be 1 when ndim == 4");
+    }
+    if (A.E < 0) return fail(SB_EARG, "blend extent along %s must be >= 0", names[a]);
+    if (A.R < 1) return fail(SB_EARG, "row limit along %s must be >= 1", names[a]);
+    A.ext.assign(tile_extents + off, tile_extents + off + A.n);
+    off += A.n;
+    for (int64_t k = 0; k < A.n; ++k) {
+      if (A.ext[k] < 1) return fail(SB_EARG, "tile extent %s[%lld] must be >= 1", names[a], (long long)k);
+      if (A.ext[k] > (int64_t)1 << 30) return fail(SB_EGEOM, "tile extent too large");
+      if (k < A.n - 1 && A.ext[k] < A.R)
+        return fail(SB_EGEOM, "non-last tile %s[%lld] = %lld is shorter than the row limit %lld",
+                    names[a], (long long)k, (long long)A.ext[k], (long long)A.R);
+    }
+    if (G.ndim == 4 && a == 0 && A.ext[0] != 1) return fail(SB_EARG, "t_0 must be 1 when ndim == 4");
+    A.e.assign(A.n, 0);
+    for (int64_t k = 1; k < A.n; ++k) A.e[k] = std::min(A.E, std::min(A.ext[k - 1], A.ext[k]));
+    for (int64_t k = 0; k < A.n; ++k) {
+      const int64_t nxt = k + 1 < A.n ? A.e[k + 1] : 0;
+      if (A.ext[k] < A.e[k] + nxt)
+        return fail(SB_EGEOM,
+                    "tile %s[%lld] = %lld is shorter than its two blend seams (%lld + %lld): the "
+                    "data-parallel closed form needs a tile's head seam and tail to be disjoint",
+                    names[a], (long long)k, (long long)A.ext[k], (long long)A.e[k], (long long)nxt);
+    }
+    A.L = (A.n - 1) * A.R + A.ext[A.n - 1];
+    if (A.L > (int64_t)1 << 30) return fail(SB_EGEOM, "output extent too large");
+  }
+  return SB_OK;
+}
+
+// --------------------------------------------------------------------------
+// device properties cached per device (no allocation)
+// --------------------------------------------------------------------------
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+} // namespace
+
+extern "C" const char *seamblend_last_error(void) { return g_err.c_str(); }
+
+extern "C" int vae_tile_blend_stitch_output_extents(const int64_t grid[6], const int64_t *tile_extents,
+                                                    const int64_t blend_extent[3],
+                                                    const int64_t row_limit[3],
+                                                    int64_t out_extents[3]) {
+  Grid G;
+  int rc = build_grid(grid, tile_extents, blend_extent, row_limit, G);
+  if (rc) return rc;
+  if (!out_extents) return fail(SB_EARG, "null out_extents");
+  for (int a = 0; a < 3; ++a) out_extents[a] = G.ax[a].L;
+  return SB_OK;
+}
+
+extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t grid[6],
+                                     const int64_t *tile_extents, const int64_t blend_extent[3],
+                                     const int64_t row_limit[3], int dtype, void *out, void *stream) {
+  Grid G;
+  int rc = build_grid(grid, tile_extents, blend_extent, row_limit, G);
+  if (rc) return rc;
+  if (dtype != SB_F32 && dtype != SB_F16 && dtype != SB_BF16)
+    return fail(SB_EARG, "unknown dtype %d", dtype);
+  const Axis &At = G.ax[0], &Ah = G.ax[1], &Aw = G.ax[2];
+  const int64_t planes = G.N * G.C;
+  const int EB = elem_bytes(dtype);
+  const int64_t ntiles = At.n * Ah.n * Aw.n;
+  if (!tiles) return fail(SB_EARG, "null tiles");
+  if (!out) return fail(SB_EARG, "null out");
+  for (int64_t k = 0; k < ntiles; ++k) {
+    if (!tiles[k]) return fail(SB_EARG, "null tile pointer %lld", (long long)k);
+    if (!aligned(tiles[k], EB)) return fail(SB_EARG, "tile %lld is not aligned to its element size", (long long)k);
+  }
+  if (!aligned(out, EB)) return fail(SB_EARG, "out is not aligned to its element size");
+  if (planes == 0) return SB_OK;
+
+  // output must not overlap any tile (address ranges)
+  const uintptr_t o0 = (uintptr_t)out;
+  const uintptr_t o1 = o0 + (uintptr_t)(planes * At.L * Ah.L * Aw.L * EB);
+  for (int64_t tau = 0; tau < At.n; ++tau)
+    for (int64_t i = 0; i < Ah.n; ++i)
+      for (int64_t j = 0; j < Aw.n; ++j) {
+        const uintptr_t t0 = (uintptr_t)tiles[(tau * Ah.n + i) * Aw.n + j];
+        const uintptr_t t1 = t0 + (uintptr_t)(planes * At.ext[tau] * Ah.ext[i] * Aw.ext[j] * EB);
+        if (t0 < o1 && o0 < t1)
+          return fail(SB_EARG, "out overlaps tile (%lld,%lld,%lld)", (long long)tau, (long long)i,
+                      (long long)j);
+      }
+
+  // vector width: 16-byte vectors when every row, row offset and seam boundary
+  // along W is a whole number of vectors and every base is 16-byte aligned
+  const int V16 = 16 / EB;
+  bool vec16 = aligned(out, 16) && Aw.L % V16 == 0 && Aw.R % V16 == 0;
+  for (int64_t k = 0; k < Aw.n && vec16; ++k) vec16 = Aw.ext[k] % V16 == 0 && Aw.e[k] % V16 == 0;
+  for (int64_t k = 0; k < ntiles && vec16; ++k) vec16 = aligned(tiles[k], 16);
+  const int V = vec16 ? V16 : 1;
+
+  const int64_t Wv = Aw.L / V;
+  if (At.L * Ah.L * Wv >= ((int64_t)1 << 31))
+    return fail(SB_EGEOM, "one (n, c) plane of the output exceeds 2^31 vectors");
+
+  // coefficient tables: one LDS segment per distinct clamped extent per axis
+  sb::BlendArgs A;
+  std::memset(&A, 0, sizeof A);
+  int32_t pool = 0;
+  for (int a = 0; a < 3; ++a) {
+    const Axis &X = G.ax[a];
+    for (int64_t k = 0; k < X.n; ++k) {
+      A.ext[a][k] = (int32_t)X.ext[k];
+      A.coff[a][k] = -1;
+      if (X.e[k] <= 0) continue;
+      int d = 0;
+      while (d < A.n_dist[a] && A.dist_e[a][d] != X.e[k]) ++d;
+      if (d == A.n_dist[a]) {
+        if (d == sb::kMaxDistinct) return fail(SB_EGEOM, "more than %d distinct blend extents on one axis", sb::kMaxDistinct);
+        if (pool + X.e[k] > sb::kMaxPoolPairs)
+          return fail(SB_EGEOM, "blend extents too large for the coefficient tables (%d pairs max)",
+                      sb::kMaxPoolPairs);
+        A.dist_e[a][d] = (int32_t)X.e[k];
+        A.dist_off[a][d] = pool;
+        pool += (int32_t)X.e[k];
+        A.n_dist[a]++;
+      }
+      A.coff[a][k] = (int16_t)A.dist_off[a][d];
+    }
+  }
+  A.pool_pairs = pool;
+  A.out = out;
+  A.n_t = (int32_t)At.n; A.n_h = (int32_t)Ah.n; A.n_w = (int32_t)Aw.n;
+  for (int a = 0; a < 3; ++a) {
+    A.E[a] = (int32_t)G.ax[a].E;
+    A.R[a] = (int32_t)G.ax[a].R;
+  }
+  A.LT = (int32_t)At.L; A.LH = (int32_t)Ah.L; A.LW = (int32_t)Aw.L;
+  A.Wv = (int32_t)Wv;
+  A.div_Wv = sb::make_fastdiv((uint32_t)Wv);
+  A.div_Rt = sb::make_fastdiv((uint32_t)At.R);
+  A.div_Rh = sb::make_fastdiv((uint32_t)Ah.R);
+  A.div_Rw = sb::make_fastdiv((uint32_t)Aw.R);
+  const size_t lds = (size_t)std::max(pool, 1) * sizeof(float2);
+  const int cus = cu_count();
+  hipStream_t st = (hipStream_t)stream;
+
+  // Launch windows.  A window covers output frames of temporal tiles
+  // [t0, t1) and rows of tile rows [i0, i1); it needs the tile pointers of
+  // temporal tiles [max(t0-1,0), t1) and tile rows [max(i0-1,0), i1).
+  // Windows are grown greedily within the kernel-argument pointer budget.
+  auto tiles_needed = [&](int64_t t0, int64_t t1, int64_t i0, int64_t i1) {
+    return (t1 - std::max<int64_t>(t0 - 1, 0)) * (i1 - std::max<int64_t>(i0 - 1, 0)) * Aw.n;
+  };
+  int64_t t0 = 0;
+  while (t0 < At.n) {
+    int64_t t1 = t0 + 1;
+    while (t1 < At.n && tiles_needed(t0, t1 + 1, 0, Ah.n) <= sb::kMaxWindowTiles) ++t1;
+    int64_t i0 = 0;
+    while (i0 < Ah.n) {
+      int64_t i1 = i0 + 1;
+      if (tiles_needed(t0, t1, i0, i1) > sb::kMaxWindowTiles)
+        return fail(SB_EGEOM, "tile grid too wide: %lld tiles per row exceed one launch window",
+                    (long long)Aw.n);
+      while (i1 < Ah.n && tiles_needed(t0, t1, i0, i1 + 1) <= sb::kMaxWindowTiles) ++i1;
+      const int64_t tb = std::max<int64_t>(t0 - 1, 0), ib = std::max<int64_t>(i0 - 1, 0);
+      A.taub = (int32_t)tb;
+      A.ib = (int32_t)ib;
+      A.ptr_nh = (int32_t)(i1 - ib);
+      for (int k = 0; k < sb::kMaxWindowTiles; ++k) A.ptr[k] = nullptr;
+      for (int64_t tq = tb; tq < t1; ++tq)
+        for (int64_t iq = ib; iq < i1; ++iq)
+          for (int64_t jq = 0; jq < Aw.n; ++jq)
+            A.ptr[((tq - tb) * A.ptr_nh + (iq - ib)) * Aw.n + jq] = tiles[(tq * Ah.n + iq) * Aw.n + jq];
+      const int64_t F0 = t0 * At.R, F1 = (t1 == At.n) ? At.L : t1 * At.R;
+      const int64_t Y0 = i0 * Ah.R, Y1 = (i1 == Ah.n) ? Ah.L : i1 * Ah.R;
+      A.F0 = (int32_t)F0; A.nF = (int32_t)(F1 - F0);
+      A.Y0 = (int32_t)Y0; A.nY = (int32_t)(Y1 - Y0);
+      A.div_nY = sb::make_fastdiv((uint32_t)A.nY);
+      A.div_nF = sb::make_fastdiv((uint32_t)A.nF);
+      const int64_t per_plane = (int64_t)A.nF * A.nY * Wv;
+      const int64_t max_planes = std::max<int64_t>(1, (((int64_t)1 << 31) - 1) / per_plane);
+      for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
+        const int64_t np = std::min(max_planes, planes - p0);
+        A.plane0 = (int32_t)p0;
+        A.total = (uint32_t)(np * per_plane);
+        const int64_t want = ((int64_t)A.total + 255) / 256;
+        const int grid_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)cus * 8));
+        hipError_t e = sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid_blocks, lds, st);
+        if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
+      }
+      i0 = i1;
+    }
+    t0 = t1;
+  }
+  return SB_OK;
+}
+
+// --------------------------------------------------------------------------
+// GroupNorm
+// --------------------------------------------------------------------------
+namespace {
+
+struct GNPlan {
+  sb::GNArgs a;
+  bool vec16 = false;
+  size_t ws_bytes = 0;
+  bool empty = false;
+};
+
+int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axis, int64_t n_patches,
+                   int dtype_bytes, bool allow_vec, GNPlan &P) {
+  if (!shape) return fail(SB_EARG, "null shape");
+  if (ndim < 3 || ndim > 5) return fail(SB_EARG, "ndim must be 3, 4 or 5 (got %d)", ndim);
+  for (int k = 0; k < ndim; ++k)
+    if (shape[k] < 0) return fail(SB_EARG, "negative extent");
+  if (groups < 1) return fail(SB_EARG, "groups must be >= 1");
+  if (shape[1] % groups != 0) return fail(SB_EARG, "C = %lld is not divisible by groups = %lld",
+                                          (long long)shape[1], (long long)groups);
+  if (split_axis < 2 || split_axis >= ndim)
+    return fail(SB_EARG, "split_axis must be a spatial axis (2..%d), got %d", ndim - 1, split_axis);
+  if (n_patches < 1 || n_patches > sb::kMaxPatches)
+    return fail(SB_EARG, "n_patches must be in 1..%d", sb::kMaxPatches);
+  sb::GNArgs &a = P.a;
+  std::memset(&a, 0, sizeof a);
+  int64_t S = 1;
+  for (int k = 2; k < ndim; ++k) S *= shape[k];
+  a.N = (int32_t)shape[0];
+  a.C = (int32_t)shape[1];
+  a.G = (int32_t)groups;
+  a.Cg = (int32_t)(shape[1] / groups);
+  a.S = S;
+  a.P = (int32_t)n_patches;
+  a.L = (int32_t)shape[split_axis];
+  int64_t inner = 1, mid = 1;
+  for (int k = split_axis + 1; k < ndim; ++k) inner *= shape[k];
+  for (int k = 2; k < split_axis; ++k) mid *= shape[k];
+  a.inner = inner;
+  a.mid = mid;
+  a.len_small = (int32_t)(a.L / n_patches);
+  a.n_big = (int32_t)(a.L % n_patches);
+  a.len_big = a.len_small + 1;
+  P.empty = shape[0] == 0 || shape[1] == 0 || S == 0;
+  if (shape[0] > ((int64_t)1 << 20) || shape[1] > ((int64_t)1 << 24))
+    return fail(SB_EGEOM, "N or C too large");
+  // vector width: every run of a patch and every plane a whole number of
+  // 16-byte vectors (base alignment is checked per call)
+  const int V16 = 16 / dtype_bytes;
+  P.vec16 = allow_vec && S % V16 == 0 && (a.L * inner) % V16 == 0 &&
+            ((int64_t)a.len_small * inner) % V16 == 0 &&
+            (a.n_big == 0 || ((int64_t)a.len_big * inner) % V16 == 0);
+  const int V = P.vec16 ? V16 : 1;
+  const int64_t group_vec = (int64_t)a.Cg * S / V;
+  if (group_vec >= ((int64_t)1 << 31)) return fail(SB_EGEOM, "a group exceeds 2^31 vectors");
+  if (S / V >= ((int64_t)1 << 40)) return fail(SB_EGEOM, "plane too large");
+  // chunks per patch: a power of two, P_pow2 * CPP <= 64 (one wavefront merges
+  // the partials of a group), at least 16384 elements per chunk; independent
+  // of dtype and vector width so the workspace size is too
+  int64_t ppow = 1;
+  while (ppow < n_patches) ppow <<= 1;
+  const int64_t patch_el = (int64_t)std::max(a.len_big, 1) * inner * a.Cg * mid;
+  int64_t cpp = 1;
+  while (cpp * 2 * ppow <= 64 && patch_el / (cpp * 2) >= 16384) cpp *= 2;
+  a.CPP = (int32_t)cpp;
+  a.log2CPP = 0;
+  while ((1 << a.log2CPP) < cpp) a.log2CPP++;
+  a.per2 = 256 * 4; // vectors per pass-2 block (256 threads x 4)
+  a.chunks2 = (int32_t)std::max<int64_t>(1, (S / V + a.per2 - 1) / a.per2);
+  P.ws_bytes = (size_t)shape[0] * groups * n_patches * cpp * 3 * sizeof(float);
+  if (P.ws_bytes == 0) P.ws_bytes = 16;
+  return SB_OK;
+}
+
+} // namespace
+
+extern "C" size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape, int64_t groups,
+                                                  int split_axis, int64_t n_patches) {
+  GNPlan P;
+  if (plan_groupnorm(ndim, shape, groups, split_axis, n_patches, 2, false, P)) return 0;
+  return P.ws_bytes;
+}
+
+extern "C" int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t groups,
+                               int split_axis, int64_t n_patches, float eps, const void *gamma,
+                               const void *beta, int dtype, void *out, void *workspace,
+                               size_t workspace_bytes, float *patch_stats, void *stream) {
+  if (dtype != SB_F32 && dtype != SB_F16 && dtype != SB_BF16)
+    return fail(SB_EARG, "unknown dtype %d", dtype);
+  GNPlan P;
+  int rc = plan_groupnorm(ndim, shape, groups, split_axis, n_patches, elem_bytes(dtype), true, P);
+  if (rc) return rc;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(SB_EARG, "eps must be finite and >= 0");
+  if (!x || !out) return fail(SB_EARG, "null x or out");
+  if (P.empty) return SB_OK;
+  if (!workspace) return fail(SB_EARG, "null workspace");
+  if (workspace_bytes < P.ws_bytes)
+    return fail(SB_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                P.ws_bytes);
+  if (!aligned(workspace, 4) || (patch_stats && !aligned(patch_stats, 4)))
+    return fail(SB_EARG, "workspace and patch_stats must be 4-byte aligned");
+  const int EB = elem_bytes(dtype);
+  if (!aligned(x, EB) || !aligned(out, EB) || (gamma && !aligned(gamma, EB)) || (beta && !aligned(beta, EB)))
+    return fail(SB_EARG, "x, out, gamma and beta must be aligned to the element size");
+  if (x != out) {
+    const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)(shape[0] * shape[1] * P.a.S * EB);
+    const uintptr_t y0 = (uintptr_t)out, y1 = y0 + (uintptr_t)(shape[0] * shape[1] * P.a.S * EB);
+    if (x0 < y1 && y0 < x1) return fail(SB_EARG, "out partially overlaps x (only exact aliasing is allowed)");
+  }
+  bool vec16 = P.vec16 && aligned(x, 16) && aligned(out, 16);
+  if (P.vec16 && !vec16) {
+    // misaligned bases: the same layout with single-element vectors
+    rc = plan_groupnorm(ndim, shape, groups, split_axis, n_patches, EB, false, P);
+    if (rc) return rc;
+  }
+  sb::GNArgs &a = P.a;
+  a.x = x;
+  a.out = out;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.part = (float *)workspace;
+  a.patch_stats = patch_stats;
+  a.eps = eps;
+  hipError_t e = sb_launch_groupnorm(a, dtype, vec16 ? 1 : 0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SB_ELAUNCH, "groupnorm launch failed: %s", hipGetErrorString(e));
+  return SB_OK;
+}

@@ -1,0 +1,241 @@
+// groupnorm.hip -- patch-split GroupNorm with Chan-merged statistics, gfx950.
+//
+// What is computed (DistVAE PR "Add tiled VAE parallelism & extended model
+// support", PatchGroupNorm commits): GroupNorm over C/G channels and all
+// spatial positions of each (n, group), with the statistics of every spatial
+// patch computed separately and merged so that the result equals unsplit
+// GroupNorm -- global mean, variance = M2 / count (no Bessel correction).
+// Patches follow the Patchify split (first L mod P patches one longer).
+//
+// Pass 1 (gn_stats_kernel): one block per (n, g, patch, chunk of the patch).
+//   Each thread accumulates a shifted sum and sum of squares about its first
+//   element (the shift keeps the fp32 sums well conditioned when the mean is
+//   large against the spread), turns them into (count, mean, M2), and the
+//   block merges those with Chan's pairwise formula
+//       d = mu_B - mu_A, n = n_A + n_B, mu = mu_A + d n_B / n,
+//       M2 = M2_A + M2_B + d^2 n_A n_B / n
+//   first across the wavefront with shuffles, then across the 4 waves in LDS.
+//   One fp32 partial (count, mean, M2) per block goes to the workspace.
+// Pass 2 (gn_norm_kernel): one block per (n, c) plane chunk.  Every wave
+//   issues its loads of x first, then merges the P x CPP partials of its group
+//   with a fixed shuffle tree (chunks of a patch first, then patches) -- the
+//   same order in every block, so results are deterministic -- and streams
+//   y = (x - mean) * (rstd * gamma_c) + beta_c back out with nontemporal
+//   stores.  Wave 0 of the first block of each group writes the optional
+//   per-patch statistics.
+
+#include "sb_internal.h"
+#include "sb_vec.h"
+
+namespace sb {
+
+struct Stat {
+  float n, mean, m2;
+};
+
+__device__ __forceinline__ Stat chan_merge(const Stat &a, const Stat &b) {
+  if (b.n == 0.f) return a;
+  if (a.n == 0.f) return b;
+  const float n = a.n + b.n;
+  const float d = b.mean - a.mean;
+  const float r = b.n / n;
+  Stat o;
+  o.n = n;
+  o.mean = a.mean + d * r;
+  o.m2 = a.m2 + b.m2 + d * d * a.n * r;
+  return o;
+}
+
+__device__ __forceinline__ Stat shfl_down_stat(const Stat &s, int o) {
+  Stat t;
+  t.n = __shfl_down(s.n, o, 64);
+  t.mean = __shfl_down(s.mean, o, 64);
+  t.m2 = __shfl_down(s.m2, o, 64);
+  return t;
+}
+
+template <int DT, int VB>
+__global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv div_big,
+                                                       FastDiv div_small) {
+  constexpr int V = VecInfo<DT, VB>::V;
+  constexpr int EB = Elem<DT>::bytes;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int c = b & (A.CPP - 1);
+  int rest = b >> A.log2CPP;
+  const int p = rest % A.P;
+  rest /= A.P;
+  const int g = rest % A.G;
+  const int n = rest / A.G;
+
+  const bool big = p < A.n_big;
+  const int len = big ? A.len_big : A.len_small;
+  const int start = big ? p * A.len_big : A.n_big * A.len_big + (p - A.n_big) * A.len_small;
+  const uint32_t runv = (uint32_t)(((int64_t)len * A.inner) / V);
+  const FastDiv dv = big ? div_big : div_small;
+  const uint32_t totalv = (uint32_t)((int64_t)A.Cg * A.mid * runv);
+  const uint32_t per = (totalv + A.CPP - 1) / A.CPP;
+  const uint32_t q0 = (uint32_t)c * per;
+  const uint32_t q1 = min(q0 + per, totalv);
+  const int64_t row = (int64_t)A.L * A.inner; // elements between consecutive runs
+  const char *gbase = (const char *)A.x +
+                      (((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S + (int64_t)start * A.inner) * EB;
+
+  float K = 0.f, s1 = 0.f, s2 = 0.f, cnt = 0.f;
+  uint32_t q = q0 + tid;
+  if (q < q1) {
+    const uint32_t r = fdiv(q, dv);
+    const uint32_t pos = q - r * runv;
+    float f[V];
+    unpack<DT, VB>(vload<VB, false>(gbase + ((int64_t)r * row + (int64_t)pos * V) * EB), f);
+    K = f[0];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const float d = f[k] - K;
+      s1 += d;
+      s2 = fmaf(d, d, s2);
+    }
+    cnt = (float)V;
+    for (q += blockDim.x; q < q1; q += blockDim.x) {
+      const uint32_t r2 = fdiv(q, dv);
+      const uint32_t pos2 = q - r2 * runv;
+      unpack<DT, VB>(vload<VB, false>(gbase + ((int64_t)r2 * row + (int64_t)pos2 * V) * EB), f);
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const float d = f[k] - K;
+        s1 += d;
+        s2 = fmaf(d, d, s2);
+      }
+      cnt += (float)V;
+    }
+  }
+  Stat st;
+  st.n = cnt;
+  if (cnt > 0.f) {
+    const float m = s1 / cnt;
+    st.mean = K + m;
+    st.m2 = fmaxf(s2 - s1 * m, 0.f);
+  } else {
+    st.mean = 0.f;
+    st.m2 = 0.f;
+  }
+  // wavefront tree, lane l merges lane l + o
+  const int lane = tid & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const Stat t = shfl_down_stat(st, o);
+    if ((lane & (2 * o - 1)) == 0 && lane + o < 64) st = chan_merge(st, t);
+  }
+  __shared__ Stat s_w[4];
+  if (lane == 0) s_w[tid >> 6] = st;
+  __syncthreads();
+  if (tid == 0) {
+    Stat m = s_w[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = chan_merge(m, s_w[w]);
+    float *dst = A.part + (int64_t)b * 3;
+    dst[0] = m.n;
+    dst[1] = m.mean;
+    dst[2] = m.m2;
+  }
+}
+
+constexpr int kNormUnroll = 4;
+
+template <int DT, int VB>
+__global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
+  constexpr int V = VecInfo<DT, VB>::V;
+  constexpr int EB = Elem<DT>::bytes;
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x;
+  const int64_t plane = blockIdx.y;
+  const int n = (int)(plane / A.C);
+  const int ch = (int)(plane - (int64_t)n * A.C);
+  const int g = ch / A.Cg;
+  const int64_t Sv = A.S / V;
+  const int64_t q0 = (int64_t)chunk * A.per2;
+  const int64_t q1 = min(q0 + A.per2, Sv);
+  const char *xb = (const char *)A.x + plane * A.S * EB;
+  char *yb = (char *)A.out + plane * A.S * EB;
+
+  // loads first, so their latency overlaps the statistics merge
+  Vec<VB> xs[kNormUnroll];
+#pragma unroll
+  for (int u = 0; u < kNormUnroll; ++u) {
+    const int64_t q = q0 + (int64_t)u * blockDim.x + tid;
+    if (q < q1) xs[u] = vload<VB, true>(xb + q * V * EB);
+  }
+
+  // merge the group's partials: lane l holds (patch l / CPP, chunk l % CPP)
+  const int lane = tid & 63;
+  const int K = A.P * A.CPP;
+  Stat st{0.f, 0.f, 0.f};
+  if (lane < K) {
+    const float *src = A.part + ((int64_t)(n * A.G + g) * K + lane) * 3;
+    st.n = src[0];
+    st.mean = src[1];
+    st.m2 = src[2];
+  }
+  const bool writer = A.patch_stats != nullptr && chunk == 0 && (ch % A.Cg) == 0 && tid < 64;
+  if (writer && A.CPP == 1 && lane < A.P) {
+    float *d = A.patch_stats + ((int64_t)(n * A.G + g) * A.P + lane) * 3;
+    d[0] = st.n; d[1] = st.mean; d[2] = st.m2;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const Stat t = shfl_down_stat(st, o);
+    if ((lane & (2 * o - 1)) == 0 && lane + o < 64) st = chan_merge(st, t);
+    if (writer && 2 * o == A.CPP && (lane & (A.CPP - 1)) == 0 && (lane >> A.log2CPP) < A.P) {
+      float *d = A.patch_stats + ((int64_t)(n * A.G + g) * A.P + (lane >> A.log2CPP)) * 3;
+      d[0] = st.n; d[1] = st.mean; d[2] = st.m2;
+    }
+  }
+  const float cnt = __shfl(st.n, 0, 64);
+  const float mean = __shfl(st.mean, 0, 64);
+  const float m2 = __shfl(st.m2, 0, 64);
+  const float var = m2 / cnt;
+  const float rstd = 1.0f / sqrtf(var + A.eps);
+  const float gam = A.gamma ? widen<DT>(DT == DT_F32 ? ((const uint32_t *)A.gamma)[ch]
+                                                     : ((const uint16_t *)A.gamma)[ch])
+                            : 1.0f;
+  const float bet = A.beta ? widen<DT>(DT == DT_F32 ? ((const uint32_t *)A.beta)[ch]
+                                                    : ((const uint16_t *)A.beta)[ch])
+                           : 0.0f;
+  const float a = rstd * gam;
+
+#pragma unroll
+  for (int u = 0; u < kNormUnroll; ++u) {
+    const int64_t q = q0 + (int64_t)u * blockDim.x + tid;
+    if (q < q1) {
+      float f[V];
+      unpack<DT, VB>(xs[u], f);
+#pragma unroll
+      for (int k = 0; k < V; ++k) f[k] = fmaf(f[k] - mean, a, bet);
+      vstore<VB, true>(yb + q * V * EB, pack<DT, VB>(f));
+    }
+  }
+}
+
+template <int DT, int VB>
+static hipError_t launch_gn(const GNArgs &a, hipStream_t st) {
+  constexpr int V = VecInfo<DT, VB>::V;
+  const int64_t rb = ((int64_t)a.len_big * a.inner) / V;
+  const int64_t rs = ((int64_t)a.len_small * a.inner) / V;
+  const FastDiv db = make_fastdiv((uint32_t)(rb > 0 ? rb : 1));
+  const FastDiv ds = make_fastdiv((uint32_t)(rs > 0 ? rs : 1));
+  const unsigned blocks1 = (unsigned)((int64_t)a.N * a.G * a.P * a.CPP);
+  hipLaunchKernelGGL((gn_stats_kernel<DT, VB>), dim3(blocks1), dim3(256), 0, st, a, db, ds);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gn_norm_kernel<DT, VB>), dim3((unsigned)a.chunks2, (unsigned)((int64_t)a.N * a.C)),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+} // namespace sb
+
+hipError_t sb_launch_groupnorm(const sb::GNArgs &a, int dtype, int vec16, hipStream_t st) {
+  using namespace sb;
+  if (dtype == DT_F32) return vec16 ? launch_gn<DT_F32, 16>(a, st) : launch_gn<DT_F32, 4>(a, st);
+  if (dtype == DT_F16) return vec16 ? launch_gn<DT_F16, 16>(a, st) : launch_gn<DT_F16, 2>(a, st);
+  return vec16 ? launch_gn<DT_BF16, 16>(a, st) : launch_gn<DT_BF16, 2>(a, st);
+}

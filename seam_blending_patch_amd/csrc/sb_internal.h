@@ -1,0 +1,90 @@
+// sb_internal.h -- shared between the host entry points and the gfx950 kernels.
+// Not part of the public ABI (that is include/seam_blend.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sb {
+
+// ---------------------------------------------------------------------------
+// Division by a run-time invariant divisor with one high multiply and a shift
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, round-up variant).  For 1 <= d < 2^31 pick
+// s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1; then for every
+// 0 <= n < 2^31:  n / d == (umulhi(n, m) + n) >> s   (the sum fits 32 bits).
+// ---------------------------------------------------------------------------
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// ---------------------------------------------------------------------------
+// blend + crop + stitch launch arguments (passed by value as kernel arguments)
+// ---------------------------------------------------------------------------
+constexpr int kMaxAxisTiles = 64;    // tiles per axis
+constexpr int kMaxWindowTiles = 160; // tile pointers per launch window
+constexpr int kMaxDistinct = 8;      // distinct clamped blend extents per axis
+constexpr int kMaxPoolPairs = 6144;  // (w_a, w_b) pairs held in LDS
+
+struct BlendArgs {
+  void *out;
+  const void *ptr[kMaxWindowTiles]; // window tiles [(tau - taub)][(i - ib)][j]
+  int32_t ext[3][kMaxAxisTiles];    // extents per axis (t, h, w), global tile index
+  int16_t coff[3][kMaxAxisTiles];   // pool offset of the coefficients of e(k)
+  int32_t dist_e[3][kMaxDistinct];  // distinct clamped extents per axis ...
+  int32_t dist_off[3][kMaxDistinct];// ... and their pool offsets
+  int32_t n_dist[3];
+  int32_t n_t, n_h, n_w;
+  int32_t E[3], R[3];
+  int32_t LT, LH, LW;               // full output extents
+  int32_t taub, ib, ptr_nh;         // pointer-table origin and tile rows in it
+  int32_t F0, nF, Y0, nY;           // output frame / row range of this window
+  int32_t Wv;                       // vectors per output row
+  int32_t plane0;                   // first (n, c) plane of this window
+  uint32_t total;                   // vectors in this window
+  FastDiv div_Wv, div_nY, div_nF, div_Rt, div_Rh, div_Rw;
+  int32_t pool_pairs;
+};
+
+// ---------------------------------------------------------------------------
+// GroupNorm launch arguments
+// ---------------------------------------------------------------------------
+constexpr int kMaxPatches = 64;
+
+struct GNArgs {
+  const void *x;
+  void *out;
+  const void *gamma;
+  const void *beta;
+  float *part;        // partials [N][G][P][CPP][3]
+  float *patch_stats; // optional [N][G][P][3]
+  int32_t N, C, G, Cg;
+  int64_t S;          // spatial elements per channel
+  int32_t P, CPP, log2CPP;
+  int32_t L;          // extent of the split axis
+  int64_t inner;      // elements per step along the split axis
+  int64_t mid;        // product of the spatial extents before the split axis
+  int32_t len_big, len_small, n_big; // patch lengths along the split axis
+  float eps;
+  // pass 2
+  int32_t chunks2;    // blocks per (n, c) plane
+  int64_t per2;       // vectors per pass-2 block
+};
+
+} // namespace sb
+
+// launchers (defined in the .hip files)
+hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, int grid, size_t lds,
+                           hipStream_t st);
+hipError_t sb_launch_groupnorm(const sb::GNArgs &a, int dtype, int vec16, hipStream_t st);

@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the library loads, exports every function the header
+declares, and rejects bad arguments and geometries on the host (before any
+device work, so these run without a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seam_blend.h")
+
+
+@pytest.fixture(scope="module")
+def sb():
+    import seam_blending_patch_amd as m  # raises if the library is not built
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents", "patch_groupnorm",
+              "patch_groupnorm_workspace_bytes", "seamblend_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(sb):
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_output_extents_for_the_benchmark_grids(sb):
+    want = {1: (1, 112, 112), 2: (1, 1024, 1024), 3: (1, 2048, 2048), 4: (49, 480, 832),
+            5: (1, 4096, 4096)}
+    for k, c in workloads.CONFIGS.items():
+        w = c.blend
+        grid = (w.ndim, w.N, w.C) + w.grid
+        ext = list(w.ext_t) + list(w.ext_h) + list(w.ext_w)
+        assert sb.vae_tile_blend_stitch_output_extents(grid, ext, w.blend, w.row_limit) == want[k]
+
+
+@pytest.mark.parametrize("grid,ext,E,R,code", [
+    ((3, 1, 3, 1, 2, 2), [1, 64, 64, 64, 64], (0, 16, 16), (1, 48, 48), -1),    # bad ndim
+    ((4, 1, 3, 2, 2, 2), [1, 1, 64, 64, 64, 64], (0, 16, 16), (1, 48, 48), -1), # n_t != 1 in 4-D
+    ((4, 1, 3, 1, 2, 2), [2, 64, 64, 64, 64], (0, 16, 16), (1, 48, 48), -1),    # t_0 != 1 in 4-D
+    ((4, 1, 3, 1, 0, 2), [1, 64, 64], (0, 16, 16), (1, 48, 48), -1),            # empty grid axis
+    ((4, 1, 3, 1, 2, 2), [1, 64, 64, 64, 64], (0, -1, 16), (1, 48, 48), -1),    # negative E
+    ((4, 1, 3, 1, 2, 2), [1, 64, 64, 64, 64], (0, 16, 16), (1, 0, 48), -1),     # R = 0
+    ((4, 1, 3, 1, 2, 2), [1, 40, 64, 64, 64], (0, 16, 16), (1, 48, 48), -2),    # non-last < R
+    ((4, 1, 3, 1, 3, 1), [1, 64, 20, 64, 64], (0, 16, 16), (1, 20, 48), -2),    # head meets tail
+    ((4, 1, 3, 1, 65, 1), [1] + [8] * 65 + [8], (0, 0, 0), (1, 8, 8), -2),      # > 64 tiles per axis
+])
+def test_geometry_validation(sb, grid, ext, E, R, code):
+    with pytest.raises(sb.SeamBlendError) as ei:
+        sb.vae_tile_blend_stitch_output_extents(grid, ext, E, R)
+    assert ei.value.code == code
+    assert len(str(ei.value)) > 20
+
+
+def test_blend_rejects_bad_pointers_and_dtype_before_any_launch(sb):
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    lib.vae_tile_blend_stitch.restype = ctypes.c_int
+    lib.seamblend_last_error.restype = ctypes.c_char_p
+    i64 = lambda v: (ctypes.c_int64 * len(v))(*v)  # noqa: E731
+    grid, ext, E, R = i64([4, 1, 3, 1, 2, 2]), i64([1, 64, 64, 64, 64]), i64([0, 16, 16]), i64([1, 48, 48])
+    fake = (ctypes.c_void_p * 4)(0x1000, 0x100000, 0x200000, 0x300000)
+    assert lib.vae_tile_blend_stitch(fake, grid, ext, E, R, 7, ctypes.c_void_p(0x900000), None) == -1
+    assert b"dtype" in lib.seamblend_last_error()
+    assert lib.vae_tile_blend_stitch(None, grid, ext, E, R, 1, ctypes.c_void_p(0x900000), None) == -1
+    assert lib.vae_tile_blend_stitch(fake, grid, ext, E, R, 1, None, None) == -1
+    nul = (ctypes.c_void_p * 4)(0x1000, 0, 0x200000, 0x300000)
+    assert lib.vae_tile_blend_stitch(nul, grid, ext, E, R, 1, ctypes.c_void_p(0x900000), None) == -1
+    # output overlapping a tile
+    assert lib.vae_tile_blend_stitch(fake, grid, ext, E, R, 1, ctypes.c_void_p(0x100010), None) == -1
+    assert b"overlap" in lib.seamblend_last_error()
+    # misaligned fp32 tile
+    mis = (ctypes.c_void_p * 4)(0x1002, 0x100000, 0x200000, 0x300000)
+    assert lib.vae_tile_blend_stitch(mis, grid, ext, E, R, 0, ctypes.c_void_p(0x900000), None) == -1
+
+
+def test_groupnorm_workspace_and_validation(sb):
+    assert sb.patch_groupnorm_workspace_bytes((1, 512, 256, 256), 32, 2, 4) > 0
+    # the workspace does not depend on dtype: one size serves all
+    a = sb.patch_groupnorm_workspace_bytes((2, 256, 512, 512), 32, 3, 8)
+    assert a == 2 * 32 * 8 * 8 * 3 * 4
+    for shape, G, axis, P in [((1, 30, 8, 8), 4, 2, 2),   # C % G
+                              ((1, 32, 8, 8), 4, 1, 2),   # axis not spatial
+                              ((1, 32, 8, 8), 4, 4, 2),   # axis out of range
+                              ((1, 32, 8, 8), 4, 2, 0),   # no patches
+                              ((1, 32, 8, 8), 4, 2, 65),  # too many patches
+                              ((1, 32), 4, 2, 1)]:        # rank
+        with pytest.raises(sb.SeamBlendError):
+            sb.patch_groupnorm_workspace_bytes(shape, G, axis, P)
+
+
+def test_groupnorm_rejects_small_workspace_and_bad_args_on_host(sb):
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    lib.patch_groupnorm.restype = ctypes.c_int
+    lib.patch_groupnorm.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    shape = (ctypes.c_int64 * 4)(1, 8, 16, 16)
+    X, Y, W = 0x10000, 0x20000, 0x30000
+    assert lib.patch_groupnorm(X, 4, shape, 4, 2, 2, 1e-6, None, None, 0, Y, W, 4, None, None) == -3
+    assert lib.patch_groupnorm(X, 4, shape, 4, 2, 2, -1.0, None, None, 0, Y, W, 4096, None, None) == -1
+    assert lib.patch_groupnorm(X, 4, shape, 4, 2, 2, 1e-6, None, None, 9, Y, W, 4096, None, None) == -1
+    assert lib.patch_groupnorm(None, 4, shape, 4, 2, 2, 1e-6, None, None, 0, Y, W, 4096, None, None) == -1
+    assert lib.patch_groupnorm(X, 4, shape, 4, 2, 2, 1e-6, None, None, 0, X + 64, W, 4096, None,
+                               None) == -1  # partial overlap of out and x
+    # empty tensors are a no-op that needs no workspace
+    empty = (ctypes.c_int64 * 4)(0, 8, 16, 16)
+    assert lib.patch_groupnorm(X, 4, empty, 4, 2, 2, 1e-6, None, None, 0, Y, None, 0, None, None) == 0

@@ -1,0 +1,171 @@
+"""GPU parity of the fused blend + crop + stitch kernel against the CPU oracle:
+bit-exact in fp32, fp16 and bf16, on the five benchmark configurations at full
+size (the launch configuration the benchmark times) and on random small grids
+that span several tiles and ragged tails, through the C ABI."""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import compare
+import oracle
+import workloads
+from gpu_util import from_dev, tile_grid, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import seam_blending_patch_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_gpu(sb, w, tiles, out=None):
+    return sb.vae_tile_blend_stitch(tile_grid(w, tiles), w.blend, w.row_limit, out=out)
+
+
+def check(sb, w, tiles, what=""):
+    _say(f"[blend] {what} {w.name} grid={w.grid} dtype={w.dtype}")
+    want = oracle.blend_workload(w, tiles)
+    got_t = run_gpu(sb, w, tiles)
+    torch.cuda.synchronize()
+    compare.assert_bitexact(from_dev(got_t, w.dtype), want, w.dtype, f"{what} {w.name}")
+    return got_t, want
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_full_size_bitexact(sb, cfg):
+    w, tiles = workloads.draw_config_blend(cfg)
+    got, want = check(sb, w, tiles, f"config {cfg}")
+    # every element written exactly once: a NaN-poisoned output is fully overwritten
+    out = torch.full_like(got, float("nan"))
+    run_gpu(sb, w, tiles, out=out)
+    torch.cuda.synchronize()
+    compare.assert_bitexact(from_dev(out, w.dtype), want, w.dtype, f"config {cfg} poisoned out")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("ndim", [4, 5])
+def test_random_grids_vector_path(sb, dtype, ndim):
+    align = 4 if dtype == "fp32" else 8
+    for seed in range(16):
+        w = workloads.random_blend_workload(1000 + seed, dtype, ndim=ndim, max_tiles=5, max_ext=96,
+                                            align=align, N=2, C=3)
+        check(sb, w, workloads.draw_tiles(w), "random-vec")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("ndim", [4, 5])
+def test_random_grids_scalar_path(sb, dtype, ndim):
+    for seed in range(12):
+        w = workloads.random_blend_workload(2000 + seed, dtype, ndim=ndim, max_tiles=4, max_ext=50,
+                                            align=1, N=1, C=2)
+        check(sb, w, workloads.draw_tiles(w), "random-scalar")
+
+
+def _wl(dtype, ext_h, ext_w, E, R, ndim=4, ext_t=(1,), Et=0, Rt=1, N=1, C=3, seed=7):
+    return workloads.BlendWorkload("edge", dtype, ndim, N, C, list(ext_t), list(ext_h), list(ext_w),
+                                   (Et, E, E), (Rt, R, R), seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_edge_cases(sb, dtype):
+    cases = [
+        _wl(dtype, [64], [64], 16, 48),                               # 1x1: plain copy
+        _wl(dtype, [64, 64, 40], [64, 64, 32], 0, 48),                # E = 0: crop + stitch
+        _wl(dtype, [40], [64, 64, 64, 16], 16, 48),                   # one tile row
+        _wl(dtype, [64, 64, 16], [64, 64, 16], 16, 48),               # slivers, e = sliver extent
+        _wl(dtype, [104] * 3, [104] * 3, 40, 32),                     # seam wider than the crop
+        _wl(dtype, [32, 32], [64, 64], 16, 16, ndim=5, ext_t=(9, 9, 1), Et=4, Rt=5),  # 1-frame tail
+        _wl(dtype, [24], [16], 8, 16, ndim=5, ext_t=(7, 7, 7, 3), Et=3, Rt=4),        # temporal only
+    ]
+    for w in cases:
+        check(sb, w, workloads.draw_tiles(w), "edge")
+
+
+def test_many_tiles_use_several_launch_windows(sb):
+    # 13 x 13 = 169 tiles exceed one launch window's pointer table
+    w = _wl("fp16", [24] * 12 + [13], [24] * 12 + [16], 8, 16, C=2)
+    check(sb, w, workloads.draw_tiles(w), "windows-2d")
+    w5 = _wl("bf16", [16] * 5 + [9], [24] * 7 + [8], 8, 16, ndim=5,
+             ext_t=(6,) * 7 + (2,), Et=2, Rt=4, C=1)
+    check(sb, w5, workloads.draw_tiles(w5), "windows-5d")
+
+
+def test_empty_batch_is_a_noop(sb):
+    w = _wl("fp16", [32, 32], [32, 32], 8, 24, N=0)
+    tiles = [np.zeros(w.tile_shape(0, i, j), np.float16) for i in range(2) for j in range(2)]
+    out = run_gpu(sb, w, tiles)
+    assert out.numel() == 0
+
+
+def test_misaligned_tiles_take_the_scalar_path(sb):
+    w = _wl("fp16", [64, 64, 32], [64, 64, 32], 16, 48, C=2)
+    tiles = workloads.draw_tiles(w)
+    want = oracle.blend_workload(w, tiles)
+    grid = tile_grid(w, tiles)
+    # re-home every tile one element past a 16-byte boundary
+    shifted = []
+    for row in grid:
+        r2 = []
+        for t in row:
+            buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+            v = buf[1:].view(t.shape)
+            v.copy_(t)
+            r2.append(v)
+        shifted.append(r2)
+    got = sb.vae_tile_blend_stitch(shifted, w.blend, w.row_limit)
+    torch.cuda.synchronize()
+    compare.assert_bitexact(from_dev(got, "fp16"), want, "fp16", "misaligned")
+
+
+def test_deterministic_and_stream_ordered(sb):
+    w, tiles = workloads.draw_config_blend(3)
+    grid = tile_grid(w, tiles)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = sb.vae_tile_blend_stitch(grid, w.blend, w.row_limit)
+        b = sb.vae_tile_blend_stitch(grid, w.blend, w.row_limit)
+    s.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_graph_replay_with_changed_inputs(sb):
+    # replays with new tile contents equal the oracle on those contents
+    w = _wl("bf16", [64, 64, 40], [64, 64, 48], 16, 48, C=3)
+    grid = tile_grid(w, workloads.draw_tiles(w))
+    flat = [t for row in grid for t in row]
+    out = sb.vae_tile_blend_stitch(grid, w.blend, w.row_limit)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sb.vae_tile_blend_stitch(grid, w.blend, w.row_limit, out=out)
+    for rep in range(3):
+        w2 = dataclasses.replace(w, seed=100 + rep)
+        new = workloads.draw_tiles(w2)
+        for t, n in zip(flat, new):
+            t.copy_(to_dev(n, "bf16").reshape(t.shape))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        compare.assert_bitexact(from_dev(out, "bf16"), oracle.blend_workload(w2, new), "bf16",
+                                f"graph replay {rep}")
+
+
+def test_rejects_bad_geometry_without_launching(sb):
+    w = _wl("fp32", [64, 30, 64], [64, 64], 16, 48)  # middle tile shorter than the row limit
+    grid = tile_grid(w, workloads.draw_tiles(w))
+    with pytest.raises(sb.SeamBlendError) as ei:
+        sb.vae_tile_blend_stitch(grid, w.blend, w.row_limit)
+    assert ei.value.code == -2

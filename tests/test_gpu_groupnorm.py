@@ -1,0 +1,133 @@
+"""GPU parity of the two-pass patch GroupNorm against the double-precision CPU
+oracle (unsplit GroupNorm), within the stated tolerances read as
+  fp32: |y - y_ref| <= 1e-5 * max(1, |y_ref|)
+  fp16 / bf16: |y - y_ref| <= max(1e-2, one step of the output type at y_ref),
+plus the per-patch statistics against the oracle's double per-patch ones."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import compare
+import oracle
+import workloads
+from gpu_util import as_f64, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import seam_blending_patch_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run(sb, gw, x, g, b, stats=False, out=None, x_dev=None):
+    xd = x_dev if x_dev is not None else to_dev(x, gw.dtype)
+    gd = None if g is None else to_dev(g, gw.dtype)
+    bd = None if b is None else to_dev(b, gw.dtype)
+    ps = None
+    if stats:
+        ps = torch.full((gw.shape[0], gw.groups, gw.n_patches, 3), float("nan"), device="cuda")
+    y = sb.patch_groupnorm(xd, gw.groups, gw.split_axis, gw.n_patches, gw.eps, gd, bd,
+                           out=out, patch_stats=ps)
+    torch.cuda.synchronize()
+    return y, ps
+
+
+def check(sb, gw, x, g, b, what=""):
+    _say(f"[gn] {what} {gw.name} shape={tuple(gw.shape)} P={gw.n_patches} axis={gw.split_axis} {gw.dtype}")
+    y, ps = run(sb, gw, x, g, b, stats=True)
+    ref, mean, var = oracle.groupnorm(x, gw.groups, gw.eps, g, b, gw.dtype)
+    ok, rep = compare.groupnorm_check(as_f64(from_dev(y, gw.dtype), gw.dtype), ref, gw.dtype)
+    _say(f"      {rep}")
+    assert ok, f"{what} {gw.name}: {rep}"
+    st = oracle.patch_stats(x, gw.groups, gw.split_axis, gw.n_patches, gw.dtype)
+    got = ps.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[..., 0], st[..., 0]), "per-patch counts"
+    scale = np.maximum(1.0, np.abs(st[..., 1]))
+    assert np.all(np.abs(got[..., 1] - st[..., 1]) <= 2e-5 * scale), "per-patch means"
+    assert np.all(np.abs(got[..., 2] - st[..., 2]) <= 1e-4 * np.maximum(st[..., 2], 1.0)), "per-patch M2"
+    return y, rep
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4, 5])
+def test_config_full_size(sb, cfg):
+    gw, (x, g, b) = workloads.draw_config_groupnorm(cfg)
+    check(sb, gw, x, g, b, f"config {cfg}")
+
+
+def _gw(shape, dtype, G, axis, P, seed, affine=True, offset=("uniform", -2.0, 2.0)):
+    return workloads.GroupNormWorkload("rand", dtype, shape, G, axis, P, 1e-6, seed, offset=offset,
+                                       affine=affine)
+
+
+CASES = [
+    ((2, 8, 16, 24), 4, 2, 3),
+    ((1, 32, 33, 40), 8, 3, 5),      # ragged patches along W
+    ((3, 6, 7, 9), 3, 2, 4),         # tiny, scalar path
+    ((1, 16, 5, 12, 16), 4, 2, 2),   # split along T
+    ((1, 16, 5, 12, 16), 4, 3, 4),   # split along H (5-D)
+    ((1, 16, 5, 12, 16), 4, 4, 8),   # split along W (5-D)
+    ((2, 12, 6, 10), 3, 2, 9),       # more patches than rows: empty patches
+    ((1, 8, 64, 64), 2, 3, 64),      # the maximum patch count
+    ((2, 4, 100), 2, 2, 3),          # 3-D
+    ((1, 64, 40, 40), 32, 2, 1),     # a single patch
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_random_shapes(sb, dtype):
+    for k, (shape, G, axis, P) in enumerate(CASES):
+        gw = _gw(shape, dtype, G, axis, P, seed=50 + k, affine=(k % 3 != 2))
+        x, g, b = workloads.draw_groupnorm(gw)
+        check(sb, gw, x, g, b, f"case {k}")
+
+
+def test_constant_group_gives_beta_exactly(sb):
+    gw = _gw((1, 16, 8, 8), "fp32", 4, 2, 2, seed=1, offset=None)
+    x = np.full(gw.shape, 2.5, np.float32)
+    g = np.linspace(0.5, 1.5, 16).astype(np.float32)
+    b = np.linspace(-1, 1, 16).astype(np.float32)
+    y, _ = run(sb, gw, x, g, b)
+    want = np.broadcast_to(b[None, :, None, None], gw.shape)
+    assert np.array_equal(from_dev(y, "fp32"), want)
+
+
+def test_in_place_and_deterministic(sb):
+    gw, (x, g, b) = workloads.draw_config_groupnorm(3)
+    y1, _ = run(sb, gw, x, g, b)
+    xd = to_dev(x, gw.dtype)
+    y2, _ = run(sb, gw, x, g, b, out=xd, x_dev=xd)
+    assert y2.data_ptr() == xd.data_ptr()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_misaligned_input_takes_the_scalar_path(sb):
+    gw = _gw((1, 16, 32, 32), "bf16", 4, 2, 4, seed=3)
+    x, g, b = workloads.draw_groupnorm(gw)
+    xd = to_dev(x, "bf16")
+    buf = torch.empty(xd.numel() + 1, dtype=xd.dtype, device=xd.device)
+    xs = buf[1:].view(xd.shape)
+    xs.copy_(xd)
+    y, _ = run(sb, gw, x, g, b, x_dev=xs)
+    ref, _, _ = oracle.groupnorm(x, gw.groups, gw.eps, g, b, "bf16")
+    ok, rep = compare.groupnorm_check(as_f64(from_dev(y, "bf16"), "bf16"), ref, "bf16")
+    assert ok, rep
+
+
+def test_workspace_too_small_is_rejected(sb):
+    x = torch.zeros((1, 8, 16, 16), device="cuda")
+    ws = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sb.SeamBlendError) as ei:
+        sb.patch_groupnorm(x, 4, 2, 2, workspace=ws)
+    assert ei.value.code == -3
