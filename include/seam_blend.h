@@ -96,6 +96,7 @@ int vae_tile_blend_stitch_output_extents(const int64_t grid[6], const int64_t *t
  * stitched temporal chunk is blended with the previous stitched chunk (as
  * already blended) along frames and cropped.  Bit-exact for every dtype.
  * Each output element is written exactly once; no scratch memory.
+ * N*C == 0 is a no-op that accepts null tile and output pointers.
  */
 int vae_tile_blend_stitch(const void *const *tiles, const int64_t grid[6],
                           const int64_t *tile_extents, const int64_t blend_extent[3],

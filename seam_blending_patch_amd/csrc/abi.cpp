@@ -145,6 +145,7 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   const int64_t planes = G.N * G.C;
   const int EB = elem_bytes(dtype);
   const int64_t ntiles = At.n * Ah.n * Aw.n;
+  if (planes == 0) return SB_OK; // nothing to read or write (empty tensors may have null data)
   if (!tiles) return fail(SB_EARG, "null tiles");
   if (!out) return fail(SB_EARG, "null out");
   for (int64_t k = 0; k < ntiles; ++k) {
@@ -152,7 +153,6 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
     if (!aligned(tiles[k], EB)) return fail(SB_EARG, "tile %lld is not aligned to its element size", (long long)k);
   }
   if (!aligned(out, EB)) return fail(SB_EARG, "out is not aligned to its element size");
-  if (planes == 0) return SB_OK;
 
   // output must not overlap any tile (address ranges)
   const uintptr_t o0 = (uintptr_t)out;
@@ -175,36 +175,21 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   for (int64_t k = 0; k < ntiles && vec16; ++k) vec16 = aligned(tiles[k], 16);
   const int V = vec16 ? V16 : 1;
 
-  const int64_t Wv = Aw.L / V;
-  if (At.L * Ah.L * Wv >= ((int64_t)1 << 31))
+  if (At.L * Ah.L * (Aw.L / V) >= ((int64_t)1 << 31))
     return fail(SB_EGEOM, "one (n, c) plane of the output exceeds 2^31 vectors");
 
-  // coefficient tables: one LDS segment per distinct clamped extent per axis
   sb::BlendArgs A;
   std::memset(&A, 0, sizeof A);
-  int32_t pool = 0;
+  int64_t ew_max = 0;
   for (int a = 0; a < 3; ++a) {
     const Axis &X = G.ax[a];
     for (int64_t k = 0; k < X.n; ++k) {
       A.ext[a][k] = (int32_t)X.ext[k];
-      A.coff[a][k] = -1;
-      if (X.e[k] <= 0) continue;
-      int d = 0;
-      while (d < A.n_dist[a] && A.dist_e[a][d] != X.e[k]) ++d;
-      if (d == A.n_dist[a]) {
-        if (d == sb::kMaxDistinct) return fail(SB_EGEOM, "more than %d distinct blend extents on one axis", sb::kMaxDistinct);
-        if (pool + X.e[k] > sb::kMaxPoolPairs)
-          return fail(SB_EGEOM, "blend extents too large for the coefficient tables (%d pairs max)",
-                      sb::kMaxPoolPairs);
-        A.dist_e[a][d] = (int32_t)X.e[k];
-        A.dist_off[a][d] = pool;
-        pool += (int32_t)X.e[k];
-        A.n_dist[a]++;
-      }
-      A.coff[a][k] = (int16_t)A.dist_off[a][d];
+      if (X.e[k] > sb::kMaxBlend)
+        return fail(SB_EGEOM, "clamped blend extent %lld exceeds %d", (long long)X.e[k], sb::kMaxBlend);
+      if (a == 2) ew_max = std::max(ew_max, X.e[k]);
     }
   }
-  A.pool_pairs = pool;
   A.out = out;
   A.n_t = (int32_t)At.n; A.n_h = (int32_t)Ah.n; A.n_w = (int32_t)Aw.n;
   for (int a = 0; a < 3; ++a) {
@@ -212,14 +197,37 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
     A.R[a] = (int32_t)G.ax[a].R;
   }
   A.LT = (int32_t)At.L; A.LH = (int32_t)Ah.L; A.LW = (int32_t)Aw.L;
-  A.Wv = (int32_t)Wv;
-  A.div_Wv = sb::make_fastdiv((uint32_t)Wv);
   A.div_Rt = sb::make_fastdiv((uint32_t)At.R);
   A.div_Rh = sb::make_fastdiv((uint32_t)Ah.R);
-  A.div_Rw = sb::make_fastdiv((uint32_t)Aw.R);
-  const size_t lds = (size_t)std::max(pool, 1) * sizeof(float2);
+  A.ew_max = (int32_t)ew_max;
+  // Rows per block.  Each block pays a fixed start-up (argument loads, seam
+  // coefficient tables, a barrier), so blocks are made as large as the
+  // problem allows while still giving every CU several blocks: about
+  // total / (cus * SB_BLEND_BLOCKS_PER_CU) vectors in the widest W segment,
+  // clamped to [1024, 8192], then balanced over the rows.
+#ifndef SB_BLEND_BLOCKS_PER_CU
+#define SB_BLEND_BLOCKS_PER_CU 8
+#endif
+  int64_t seg_max = 1;
+  for (int64_t k = 0; k < Aw.n; ++k) {
+    const int64_t crop = k < Aw.n - 1 ? Aw.R : Aw.ext[k];
+    const int64_t es = std::min(Aw.e[k], crop);
+    seg_max = std::max(seg_max, std::max(es, crop - es) / V);
+  }
   const int cus = cu_count();
+  const int64_t total_vec = planes * At.L * Ah.L * (Aw.L / V);
+  const int64_t per_block =
+      std::min<int64_t>(8192, std::max<int64_t>(1024, total_vec / ((int64_t)cus * SB_BLEND_BLOCKS_PER_CU)));
+  int64_t rows_pb = std::max<int64_t>(1, std::min<int64_t>(1024, per_block / seg_max));
+  rows_pb = std::min<int64_t>(rows_pb, Ah.L);
+  {
+    const int64_t nrb = (Ah.L + rows_pb - 1) / rows_pb;
+    rows_pb = (Ah.L + nrb - 1) / nrb;
+  }
+  A.rows_per_block = (int32_t)rows_pb;
+  const size_t lds = (size_t)(ew_max + rows_pb) * sizeof(float2);
   hipStream_t st = (hipStream_t)stream;
+  const int64_t n_wseg = 2 * Aw.n - 1;
 
   // Launch windows.  A window covers output frames of temporal tiles
   // [t0, t1) and rows of tile rows [i0, i1); it needs the tile pointers of
@@ -252,17 +260,15 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
       const int64_t Y0 = i0 * Ah.R, Y1 = (i1 == Ah.n) ? Ah.L : i1 * Ah.R;
       A.F0 = (int32_t)F0; A.nF = (int32_t)(F1 - F0);
       A.Y0 = (int32_t)Y0; A.nY = (int32_t)(Y1 - Y0);
-      A.div_nY = sb::make_fastdiv((uint32_t)A.nY);
       A.div_nF = sb::make_fastdiv((uint32_t)A.nF);
-      const int64_t per_plane = (int64_t)A.nF * A.nY * Wv;
-      const int64_t max_planes = std::max<int64_t>(1, (((int64_t)1 << 31) - 1) / per_plane);
+      const int64_t row_blocks = (A.nY + rows_pb - 1) / rows_pb;
+      // grid x = (plane, frame) pairs of this window, y = W segments, z = row bands
+      const int64_t max_planes = std::max<int64_t>(1, ((int64_t)1 << 30) / A.nF);
       for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
         const int64_t np = std::min(max_planes, planes - p0);
         A.plane0 = (int32_t)p0;
-        A.total = (uint32_t)(np * per_plane);
-        const int64_t want = ((int64_t)A.total + 255) / 256;
-        const int grid_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)cus * 8));
-        hipError_t e = sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid_blocks, lds, st);
+        const dim3 grid((unsigned)(np * A.nF), (unsigned)n_wseg, (unsigned)row_blocks);
+        hipError_t e = sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid, lds, st);
         if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
       }
       i0 = i1;

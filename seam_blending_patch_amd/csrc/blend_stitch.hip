@@ -10,10 +10,10 @@
 // and the pieces are stitched.  Temporal tiles are stitched spatially first,
 // then blended along frames against the previous stitched chunk.
 //
-// How: the in-place raster recursion has a closed form.  Given that no tile's
-// head seam meets its own tail (ext(k) >= e(k) + e(k+1)), the neighbour
-// operands read by a seam are untouched by their own blends except for one
-// corner term, so each output element needs at most 4 tiles in 2-D:
+// The in-place raster recursion has a closed form.  Given that no tile's head
+// seam meets its own tail (ext(k) >= e(k) + e(k+1)), the neighbour operands a
+// seam reads are untouched by their own blends except for one corner term, so
+// each output element needs at most 4 tiles in 2-D:
 //
 //   s  = D[i][j][y, x]
 //   if y < e_h(i):  U  = D[i-1][j][u+y, x]
@@ -23,20 +23,45 @@
 //                   if y < e_h(i): Lf = b(D[i-1][j-1][u+y, l+x], Lf; y, e_h(i))
 //                   s  = b(Lf, s; x, e_w(j))
 //
-// with u = h(i-1) - e_h(i), l = w(j-1) - e_w(j), and for frames f < e_t(tau)
-// of a temporal tile the same spatial value is taken in both chunks and
-// crossfaded, b(S_{tau-1}[t(tau-1) - e_t + f], S_tau[f]; f, e_t): 8 reads.
+// with u = h(i-1) - e_h(i), l = w(j-1) - e_w(j); for frames f < e_t(tau) the
+// same spatial value is taken in chunks tau-1 (frame t(tau-1) - e_t + f) and
+// tau, and crossfaded along frames: 8 reads.
 //
-// One thread owns one 16-byte output vector at a time (grid-stride loop over
-// the output of one launch window), reads every tile element it needs exactly
-// once (the corner operand twice from registers), and writes its output once
-// with a nontemporal store.  Interior vectors are a plain bit copy.  The
-// coefficient tables are built per block in LDS from float64 division.
-// Every product and sum is a separate fp32 operation (the library is built
-// with -ffp-contract=off), matching the per-product rounding rule exactly.
+// Work layout.  Along W every tile j contributes a seam segment (its first
+// min(e_w, crop) columns) and a body segment (the rest of its crop); along H
+// likewise per tile row; along T per frame.  A block owns one output frame of
+// one (n, c) plane, one W segment and a band of output rows (the frame index
+// varies fastest over the grid, so blocks resident together mix frames with
+// and without frame seams, spreading the heavy ones), so the column
+// tile, the column seam class, the temporal tile and the frame seam class are
+// block-uniform; the band is split at tile-row seam boundaries into runs whose
+// row class is block-uniform too.  Each run therefore executes one specialised
+// path with scalar tile base addresses, no lane divergence, and a batch of
+// output vectors per thread sized so that about eight 16-byte loads per lane
+// are in flight (interior copy: 8 vectors; row or column seam: 4; corner: 2;
+// with a frame seam, half of that).  Every tile element the output needs is
+// read once (the corner operand once, used twice), every output element is
+// written once, both with nontemporal hints.  The coefficient tables of the
+// block's seams are built in LDS from float64 division.  Every product and
+// sum is a separate fp32 operation (see crossfade below).
 
 #include "sb_internal.h"
 #include "sb_vec.h"
+
+#ifndef SB_BLEND_NT
+#define SB_BLEND_NT 1 // nontemporal hints on tile loads (each tile element is read once)
+#endif
+#ifndef SB_BLEND_LOADS
+#define SB_BLEND_LOADS 8 // 16-byte loads per lane in flight per batch
+#endif
+#ifndef SB_BLEND_WAVES_PER_EU
+#define SB_BLEND_WAVES_PER_EU 0 // occupancy hint (0: none)
+#endif
+#if SB_BLEND_WAVES_PER_EU > 0
+#define SB_BLEND_OCC __attribute__((amdgpu_waves_per_eu(SB_BLEND_WAVES_PER_EU)))
+#else
+#define SB_BLEND_OCC
+#endif
 
 namespace sb {
 
@@ -63,152 +88,333 @@ __device__ __forceinline__ float crossfade(float a, float b, float2 c) {
   return rn<DT>(pa + pb);
 }
 
-template <int DT, int VB>
-__global__ __launch_bounds__(256) void blend_stitch_kernel(const BlendArgs A) {
+// Crossfade of a packed pair of 16-bit elements: the products a*w_a and b*w_b
+// of both elements are fp32 multiplies (kept opaque as above), each pair of
+// products is rounded to the storage type by one packed conversion, and the
+// two rounded products are summed with one rounding to the storage type.
+// Same arithmetic as crossfade() element by element, fewer instructions.
+template <int DT>
+__device__ __forceinline__ uint32_t crossfade2(uint32_t a, uint32_t b, f32x2 wa, f32x2 wb) {
+  const f32x2 fa = widen2<DT>(a), fb = widen2<DT>(b);
+  f32x2 pa, pb;
+  pa.x = fa.x * wa.x;
+  pa.y = fa.y * wa.y;
+  pb.x = fb.x * wb.x;
+  pb.y = fb.y * wb.y;
+  asm("" : "+v"(pa.x), "+v"(pa.y), "+v"(pb.x), "+v"(pb.y));
+  return add2<DT>(narrow2<DT>(pa), narrow2<DT>(pb));
+}
+
+__device__ __forceinline__ float2 coefficients(int k, int e) {
+  const double q = (double)k / (double)e;
+  return make_float2((float)(1.0 - q), (float)q);
+}
+
+// Block-uniform description of one run of rows (one tile row, one row class).
+struct Run {
+  const char *m, *u, *l, *c;     // tiles (i,j), (i-1,j), (i,j-1), (i-1,j-1) of chunk tau, each
+                                 // offset so that operand (y, x) is base + y*pitch + x*EB
+  const char *pm, *pu, *pl, *pc; // the same in chunk tau-1 (frame seams)
+  int64_t pitch_j, pitch_p;      // bytes per row of tile column j and j-1
+  char *o;                       // output at (row of local y = 0, first column of the segment)
+  int64_t opitch;                // bytes per output row
+  int y0, y1;                    // local rows [y0, y1) of tile row i
+  int x0, wv;                    // first local column of the segment, vectors per row
+  float inv_wv;
+  const float2 *ch;              // row coefficients, indexed by local row (row seams)
+  const float2 *cw;              // column coefficients, indexed by local column (column seams)
+  float2 ct;                     // frame coefficient (frame seams)
+};
+
+template <int DT, int VB, bool HS, bool WS, bool TS>
+__device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
-  extern __shared__ float2 s_pool[];
-  __shared__ const char *s_ptr[kMaxWindowTiles];
-  __shared__ int32_t s_ext[3][kMaxAxisTiles];
-  __shared__ int32_t s_coff[3][kMaxAxisTiles];
+  constexpr int L = (1 + (HS ? 1 : 0) + (WS ? 1 : 0) + (HS && WS ? 1 : 0)) * (TS ? 2 : 1);
+  constexpr int U = L >= SB_BLEND_LOADS ? 1 : SB_BLEND_LOADS / L; // output vectors per thread per batch
+  const int nvec = (R.y1 - R.y0) * R.wv;
 
-  const int tid = threadIdx.x;
-  for (int k = tid; k < kMaxWindowTiles; k += blockDim.x) s_ptr[k] = (const char *)A.ptr[k];
-  for (int k = tid; k < 3 * kMaxAxisTiles; k += blockDim.x) {
-    s_ext[k / kMaxAxisTiles][k % kMaxAxisTiles] = A.ext[k / kMaxAxisTiles][k % kMaxAxisTiles];
-    s_coff[k / kMaxAxisTiles][k % kMaxAxisTiles] = A.coff[k / kMaxAxisTiles][k % kMaxAxisTiles];
+  for (int q0 = tid; q0 < nvec; q0 += nthreads * U) {
+    Vec<VB> m[U], up[U], lf[U], cn[U], pm[U], pu[U], pl[U], pc[U];
+    int yy[U], xx[U];
+    bool ok[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int q = q0 + k * nthreads;
+      ok[k] = q < nvec;
+      // row = q / wv exactly: the float quotient is within one of it for q < 2^24
+      int r = (int)((float)q * R.inv_wv);
+      r -= (r * R.wv > q) ? 1 : 0;
+      r += ((r + 1) * R.wv <= q) ? 1 : 0;
+      const int y = R.y0 + r;
+      const int x = R.x0 + (q - r * R.wv) * V;
+      yy[k] = y;
+      xx[k] = x;
+      const int64_t oj = (int64_t)y * R.pitch_j + (int64_t)x * EB;
+      const int64_t op = (int64_t)y * R.pitch_p + (int64_t)x * EB;
+      if (ok[k]) {
+        m[k] = vload<VB, SB_BLEND_NT>(R.m + oj);
+        if constexpr (HS) up[k] = vload<VB, SB_BLEND_NT>(R.u + oj);
+        if constexpr (WS) lf[k] = vload<VB, SB_BLEND_NT>(R.l + op);
+        if constexpr (HS && WS) cn[k] = vload<VB, SB_BLEND_NT>(R.c + op);
+        if constexpr (TS) {
+          pm[k] = vload<VB, SB_BLEND_NT>(R.pm + oj);
+          if constexpr (HS) pu[k] = vload<VB, SB_BLEND_NT>(R.pu + oj);
+          if constexpr (WS) pl[k] = vload<VB, SB_BLEND_NT>(R.pl + op);
+          if constexpr (HS && WS) pc[k] = vload<VB, SB_BLEND_NT>(R.pc + op);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      if (!ok[k]) continue;
+      char *dst = R.o + (int64_t)yy[k] * R.opitch + (int64_t)(xx[k] - R.x0) * EB;
+      if constexpr (!HS && !WS && !TS) {
+        vstore<VB, true>(dst, m[k]);
+      } else if constexpr (DT != DT_F32 && VB == 16) {
+        // packed pairs of 16-bit elements
+        constexpr int NW = Vec<VB>::NW;
+        f32x2 ha, hb; // row coefficients (one per row, both lanes)
+        if constexpr (HS) {
+          const float2 c = R.ch[yy[k]];
+          ha.x = ha.y = c.x;
+          hb.x = hb.y = c.y;
+        }
+        f32x2 wa[NW], wb[NW]; // column coefficients of elements 2w, 2w+1
+        if constexpr (WS) {
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const float2 c0 = R.cw[xx[k] + 2 * w], c1 = R.cw[xx[k] + 2 * w + 1];
+            wa[w].x = c0.x; wa[w].y = c1.x;
+            wb[w].x = c0.y; wb[w].y = c1.y;
+          }
+        }
+        auto spatial2 = [&](const Vec<VB> &vm, const Vec<VB> &vu, const Vec<VB> &vl,
+                            const Vec<VB> &vc, Vec<VB> &o) {
+          o = vm;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            uint32_t s = vm.w[w];
+            if constexpr (HS) {
+              uint32_t Uw = vu.w[w];
+              if constexpr (WS) Uw = crossfade2<DT>(vc.w[w], Uw, wa[w], wb[w]);
+              s = crossfade2<DT>(Uw, s, ha, hb);
+            }
+            if constexpr (WS) {
+              uint32_t Lw = vl.w[w];
+              if constexpr (HS) Lw = crossfade2<DT>(vc.w[w], Lw, ha, hb);
+              s = crossfade2<DT>(Lw, s, wa[w], wb[w]);
+            }
+            o.w[w] = s;
+          }
+        };
+        Vec<VB> S;
+        spatial2(m[k], up[k], lf[k], cn[k], S);
+        if constexpr (TS) {
+          Vec<VB> Sp;
+          spatial2(pm[k], pu[k], pl[k], pc[k], Sp);
+          f32x2 ta, tb;
+          ta.x = ta.y = R.ct.x;
+          tb.x = tb.y = R.ct.y;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) S.w[w] = crossfade2<DT>(Sp.w[w], S.w[w], ta, tb);
+        }
+        vstore<VB, true>(dst, S);
+      } else {
+        float2 chh = make_float2(0.f, 0.f);
+        if constexpr (HS) chh = R.ch[yy[k]];
+        float2 cww[V];
+        if constexpr (WS) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) cww[e] = R.cw[xx[k] + e];
+        }
+        // closed form of the spatial blends for one chunk
+        auto spatial = [&](const Vec<VB> &vm, const Vec<VB> &vu, const Vec<VB> &vl,
+                           const Vec<VB> &vc, float *o) {
+          unpack<DT, VB>(vm, o);
+          if constexpr (HS) {
+            float Uv[V];
+            unpack<DT, VB>(vu, Uv);
+            if constexpr (WS) {
+              float Cn[V];
+              unpack<DT, VB>(vc, Cn);
+#pragma unroll
+              for (int e = 0; e < V; ++e) Uv[e] = crossfade<DT>(Cn[e], Uv[e], cww[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) o[e] = crossfade<DT>(Uv[e], o[e], chh);
+          }
+          if constexpr (WS) {
+            float Lf[V];
+            unpack<DT, VB>(vl, Lf);
+            if constexpr (HS) {
+              float Cn[V];
+              unpack<DT, VB>(vc, Cn);
+#pragma unroll
+              for (int e = 0; e < V; ++e) Lf[e] = crossfade<DT>(Cn[e], Lf[e], chh);
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) o[e] = crossfade<DT>(Lf[e], o[e], cww[e]);
+          }
+        };
+        float S[V];
+        spatial(m[k], up[k], lf[k], cn[k], S);
+        if constexpr (TS) {
+          float Sp[V];
+          spatial(pm[k], pu[k], pl[k], pc[k], Sp);
+#pragma unroll
+          for (int e = 0; e < V; ++e) S[e] = crossfade<DT>(Sp[e], S[e], R.ct);
+        }
+        vstore<VB, true>(dst, pack<DT, VB>(S));
+      }
+    }
   }
-  // coefficient tables: w_b = fp32(y / e), w_a = fp32(1 - y / e), from double
-  for (int a = 0; a < 3; ++a)
-    for (int d = 0; d < A.n_dist[a]; ++d) {
-      const int e = A.dist_e[a][d], off = A.dist_off[a][d];
-      for (int y = tid; y < e; y += blockDim.x) {
-        double q = (double)y / (double)e;
-        s_pool[off + y] = make_float2((float)(1.0 - q), (float)q);
-      }
-    }
-  __syncthreads();
+}
 
+template <int DT, int VB>
+__global__ __launch_bounds__(256) SB_BLEND_OCC void blend_stitch_kernel(const BlendArgs A) {
+  constexpr int V = VecInfo<DT, VB>::V;
+  constexpr int EB = Elem<DT>::bytes;
+  extern __shared__ float2 s_tab[]; // [ew_max] column coefficients, then [rows_per_block] row ones
+  const int tid = threadIdx.x, nthr = blockDim.x;
   const int nw = A.n_w, nh = A.n_h, nt = A.n_t;
-  const int Eh = A.E[1], Ew = A.E[2], Et = A.E[0];
-  const int Rt = A.R[0], Rh = A.R[1], Rw = A.R[2];
-  const uint32_t stride = gridDim.x * blockDim.x;
-  char *const out = (char *)A.out;
 
-  for (uint32_t g = blockIdx.x * blockDim.x + tid; g < A.total; g += stride) {
-    // output coordinates of this vector
-    const uint32_t line = fdiv(g, A.div_Wv);
-    const int xv = (int)(g - line * (uint32_t)A.Wv);
-    const uint32_t l2 = fdiv(line, A.div_nY);
-    const int r = (int)(line - l2 * (uint32_t)A.nY);
-    const uint32_t pl = fdiv(l2, A.div_nF);
-    const int fo = (int)(l2 - pl * (uint32_t)A.nF);
-    const int64_t plane = (int64_t)A.plane0 + pl;
-    const int y_out = A.Y0 + r, f_out = A.F0 + fo, x_out = xv * V;
-    // tile cell and local coordinates
-    const int i = min((int)fdiv((uint32_t)y_out, A.div_Rh), nh - 1);
-    const int y = y_out - i * Rh;
-    const int tau = min((int)fdiv((uint32_t)f_out, A.div_Rt), nt - 1);
-    const int f = f_out - tau * Rt;
-    const int j = min((int)fdiv((uint32_t)x_out, A.div_Rw), nw - 1);
-    const int x = x_out - j * Rw;
+  // ---- W segment: tile column j, seam or body (block-uniform) ----
+  const int sw = blockIdx.y; // grid: x = (plane, frame), y = W segment, z = row band
+  const int j = (sw + 1) >> 1;
+  const bool wseam = (sw & 1) != 0;
+  const int wj = A.ext[2][j];
+  const int wp = j > 0 ? A.ext[2][j - 1] : 0;
+  const int ew = j > 0 ? min(A.E[2], min(wp, wj)) : 0;
+  const int cw = j < nw - 1 ? A.R[2] : wj;
+  const int ews = min(ew, cw);
+  const int x0 = wseam ? 0 : ews;
+  const int x1 = wseam ? ews : cw;
+  if (x1 <= x0) return; // empty segment (no seam, or a tile that is all seam)
 
-    const int hi = s_ext[1][i], wj = s_ext[2][j];
-    const int hp = i > 0 ? s_ext[1][i - 1] : 0;
-    const int wp = j > 0 ? s_ext[2][j - 1] : 0;
-    const int eh = i > 0 ? min(Eh, min(hp, hi)) : 0;
-    const int ew = j > 0 ? min(Ew, min(wp, wj)) : 0;
-    const int tp = tau > 0 ? s_ext[0][tau - 1] : 0;
-    const int et = tau > 0 ? min(Et, min(tp, s_ext[0][tau])) : 0;
-    const bool hs = y < eh, ws = x < ew, ts = f < et;
+  // ---- frame: temporal tile tau, local frame f (block-uniform) ----
+  const uint32_t pz = blockIdx.x;
+  const uint32_t pli = fdiv(pz, A.div_nF);
+  const int64_t plane = (int64_t)A.plane0 + pli;
+  const int f_out = A.F0 + (int)(pz - pli * (uint32_t)A.nF);
+  const int tau = min((int)fdiv((uint32_t)f_out, A.div_Rt), nt - 1);
+  const int f = f_out - tau * A.R[0];
+  const int tt = A.ext[0][tau];
+  const int tp = tau > 0 ? A.ext[0][tau - 1] : 0;
+  const int et = tau > 0 ? min(A.E[0], min(tp, tt)) : 0;
+  const bool ts = f < et;
+  const int fp = tp - et + f; // frame of chunk tau-1 blended into frame f
 
-    const int64_t o_off = (((plane * A.LT + f_out) * A.LH + y_out) * (int64_t)A.LW + x_out) * EB;
+  // ---- output rows of this block ----
+  const int r0 = blockIdx.z * A.rows_per_block;
+  const int r1 = min(r0 + A.rows_per_block, A.nY);
+  const int yo0 = A.Y0 + r0, yo1 = A.Y0 + r1;
 
-    // address of tile (tq, ti, tj) element (plane, fq, yq, xq)
-    auto tile_at = [&](int tq, int ti, int tj, int tt, int th, int tw, int fq, int yq, int xq) {
-      const char *base = s_ptr[((tq - A.taub) * A.ptr_nh + (ti - A.ib)) * nw + tj];
-      return base + ((((plane * tt + fq) * th + yq) * (int64_t)tw + xq) * EB);
-    };
-
-    if (!(hs || ws || ts)) {
-      const Vec<VB> s = vload<VB, true>(tile_at(tau, i, j, s_ext[0][tau], hi, wj, f, y, x));
-      vstore<VB, true>(out + o_off, s);
-      continue;
-    }
-
-    const int u = hs ? hp - eh : 0;
-    const int l = ws ? wp - ew : 0;
-    float2 chh = make_float2(0.f, 0.f);
-    if (hs) chh = s_pool[s_coff[1][i] + y];
-    float2 cww[V];
-    if (ws) {
-#pragma unroll
-      for (int k = 0; k < V; ++k) cww[k] = s_pool[s_coff[2][j] + x + k];
-    }
-
-    // spatially stitched value of chunk tq at frame fq (closed form above)
-    auto spatial = [&](int tq, int fq, float *o) {
-      const int tt = s_ext[0][tq];
-      Vec<VB> vs, vu, vl, vc;
-      vs = vload<VB, true>(tile_at(tq, i, j, tt, hi, wj, fq, y, x));
-      if (hs) vu = vload<VB, true>(tile_at(tq, i - 1, j, tt, hp, wj, fq, u + y, x));
-      if (ws) vl = vload<VB, true>(tile_at(tq, i, j - 1, tt, hi, wp, fq, y, l + x));
-      if (hs && ws) vc = vload<VB, true>(tile_at(tq, i - 1, j - 1, tt, hp, wp, fq, u + y, l + x));
-      unpack<DT, VB>(vs, o);
-      if (hs) {
-        float U[V];
-        unpack<DT, VB>(vu, U);
-        if (ws) {
-          float Cn[V];
-          unpack<DT, VB>(vc, Cn);
-#pragma unroll
-          for (int k = 0; k < V; ++k) U[k] = crossfade<DT>(Cn[k], U[k], cww[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < V; ++k) o[k] = crossfade<DT>(U[k], o[k], chh);
+  // ---- coefficient tables (only the ones this block's seams use) ----
+  float2 *s_cw = s_tab;
+  float2 *s_ch = s_tab + A.ew_max;
+  bool tables = wseam;
+  if (wseam)
+    for (int x = tid; x < ews; x += nthr) s_cw[x] = coefficients(x, ew);
+  if (A.E[1] > 0) {
+    // does the row band meet a row seam?  (block-uniform)
+    const int ia = min((int)fdiv((uint32_t)yo0, A.div_Rh), nh - 1);
+    const int ib2 = min((int)fdiv((uint32_t)(yo1 - 1), A.div_Rh), nh - 1);
+    const int ylo = yo0 - ia * A.R[1];
+    const bool meets = ib2 > ia || (ia > 0 && ylo < min(A.E[1], min(A.ext[1][ia - 1], A.ext[1][ia])));
+    if (meets) {
+      tables = true;
+      for (int k = tid; k < r1 - r0; k += nthr) {
+        const int yo = yo0 + k;
+        const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
+        const int y = yo - i * A.R[1];
+        const int eh = i > 0 ? min(A.E[1], min(A.ext[1][i - 1], A.ext[1][i])) : 0;
+        if (y < eh) s_ch[k] = coefficients(y, eh);
       }
-      if (ws) {
-        float Lf[V];
-        unpack<DT, VB>(vl, Lf);
-        if (hs) {
-          float Cn[V];
-          unpack<DT, VB>(vc, Cn);
-#pragma unroll
-          for (int k = 0; k < V; ++k) Lf[k] = crossfade<DT>(Cn[k], Lf[k], chh);
-        }
-#pragma unroll
-        for (int k = 0; k < V; ++k) o[k] = crossfade<DT>(Lf[k], o[k], cww[k]);
-      }
-    };
+    }
+  }
+  const float2 ct = ts ? coefficients(f, et) : make_float2(0.f, 0.f);
+  if (tables) __syncthreads();
 
-    float S[V];
-    spatial(tau, f, S);
+  const char *const *P = (const char *const *)A.ptr;
+  auto tile = [&](int tq, int ti, int tj) {
+    return P[((tq - A.taub) * A.ptr_nh + (ti - A.ib)) * nw + tj];
+  };
+
+  // ---- runs of rows with one tile row and one row class ----
+  int yo = yo0;
+  while (yo < yo1) {
+    const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
+    const int ybase = i * A.R[1];
+    const int hi = A.ext[1][i];
+    const int hp = i > 0 ? A.ext[1][i - 1] : 0;
+    const int eh = i > 0 ? min(A.E[1], min(hp, hi)) : 0;
+    const int chh = i < nh - 1 ? A.R[1] : hi;
+    const int ehs = min(eh, chh);
+    const int yl = yo - ybase;
+    const bool hs = yl < ehs;
+    const int yl1 = min(hs ? ehs : chh, yl + (yo1 - yo));
+
+    Run R;
+    const int u = hp - eh, l = wp - ew;
+    // plane, frame and neighbour-tail offsets folded into the tile bases
+    const int64_t pj = (int64_t)wj * EB, pp = (int64_t)wp * EB;
+    R.pitch_j = pj;
+    R.pitch_p = pp;
+    R.m = tile(tau, i, j) + ((plane * tt + f) * hi) * pj;
+    R.u = R.l = R.c = R.pm = R.pu = R.pl = R.pc = nullptr;
+    if (hs) R.u = tile(tau, i - 1, j) + ((plane * tt + f) * hp + u) * pj;
+    if (wseam) R.l = tile(tau, i, j - 1) + ((plane * tt + f) * hi) * pp + (int64_t)l * EB;
+    if (hs && wseam) R.c = tile(tau, i - 1, j - 1) + ((plane * tt + f) * hp + u) * pp + (int64_t)l * EB;
     if (ts) {
-      float Sp[V];
-      spatial(tau - 1, tp - et + f, Sp);
-      const float2 ct = s_pool[s_coff[0][tau] + f];
-#pragma unroll
-      for (int k = 0; k < V; ++k) S[k] = crossfade<DT>(Sp[k], S[k], ct);
+      R.pm = tile(tau - 1, i, j) + ((plane * tp + fp) * hi) * pj;
+      if (hs) R.pu = tile(tau - 1, i - 1, j) + ((plane * tp + fp) * hp + u) * pj;
+      if (wseam) R.pl = tile(tau - 1, i, j - 1) + ((plane * tp + fp) * hi) * pp + (int64_t)l * EB;
+      if (hs && wseam)
+        R.pc = tile(tau - 1, i - 1, j - 1) + ((plane * tp + fp) * hp + u) * pp + (int64_t)l * EB;
     }
-    vstore<VB, true>(out + o_off, pack<DT, VB>(S));
+    R.opitch = (int64_t)A.LW * EB;
+    R.o = (char *)A.out + (((plane * A.LT + f_out) * A.LH + ybase) * (int64_t)A.LW +
+                           (int64_t)j * A.R[2] + x0) * EB;
+    R.y0 = yl;
+    R.y1 = yl1;
+    R.x0 = x0;
+    R.wv = (x1 - x0) / V;
+    R.inv_wv = 1.0f / (float)R.wv;
+    R.ch = s_ch + (ybase - yo0); // R.ch[y]: coefficient of local row y (output row ybase + y)
+    R.cw = s_cw;
+    R.ct = ct;
+
+    const int cls = (ts ? 4 : 0) | (hs ? 2 : 0) | (wseam ? 1 : 0);
+    switch (cls) {
+      case 0: run_rows<DT, VB, false, false, false>(R, tid, nthr); break;
+      case 1: run_rows<DT, VB, false, true, false>(R, tid, nthr); break;
+      case 2: run_rows<DT, VB, true, false, false>(R, tid, nthr); break;
+      case 3: run_rows<DT, VB, true, true, false>(R, tid, nthr); break;
+      case 4: run_rows<DT, VB, false, false, true>(R, tid, nthr); break;
+      case 5: run_rows<DT, VB, false, true, true>(R, tid, nthr); break;
+      case 6: run_rows<DT, VB, true, false, true>(R, tid, nthr); break;
+      default: run_rows<DT, VB, true, true, true>(R, tid, nthr); break;
+    }
+    yo += yl1 - yl;
   }
 }
 
 } // namespace sb
 
-hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, int grid, size_t lds,
+hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                            hipStream_t st) {
   using namespace sb;
-  dim3 g(grid), b(256);
+  dim3 b(256);
   if (dtype == DT_F32) {
-    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_F32, 16>), g, b, lds, st, a);
-    else hipLaunchKernelGGL((blend_stitch_kernel<DT_F32, 4>), g, b, lds, st, a);
+    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_F32, 16>), grid, b, lds, st, a);
+    else hipLaunchKernelGGL((blend_stitch_kernel<DT_F32, 4>), grid, b, lds, st, a);
   } else if (dtype == DT_F16) {
-    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_F16, 16>), g, b, lds, st, a);
-    else hipLaunchKernelGGL((blend_stitch_kernel<DT_F16, 2>), g, b, lds, st, a);
+    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_F16, 16>), grid, b, lds, st, a);
+    else hipLaunchKernelGGL((blend_stitch_kernel<DT_F16, 2>), grid, b, lds, st, a);
   } else {
-    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_BF16, 16>), g, b, lds, st, a);
-    else hipLaunchKernelGGL((blend_stitch_kernel<DT_BF16, 2>), g, b, lds, st, a);
+    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_BF16, 16>), grid, b, lds, st, a);
+    else hipLaunchKernelGGL((blend_stitch_kernel<DT_BF16, 2>), grid, b, lds, st, a);
   }
   return hipGetLastError();
 }

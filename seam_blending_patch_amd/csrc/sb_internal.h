@@ -33,28 +33,22 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
 // blend + crop + stitch launch arguments (passed by value as kernel arguments)
 // ---------------------------------------------------------------------------
 constexpr int kMaxAxisTiles = 64;    // tiles per axis
-constexpr int kMaxWindowTiles = 160; // tile pointers per launch window
-constexpr int kMaxDistinct = 8;      // distinct clamped blend extents per axis
-constexpr int kMaxPoolPairs = 6144;  // (w_a, w_b) pairs held in LDS
+constexpr int kMaxWindowTiles = 192; // tile pointers per launch window
+constexpr int kMaxBlend = 4096;      // largest clamped blend extent (LDS coefficient tables)
 
 struct BlendArgs {
   void *out;
   const void *ptr[kMaxWindowTiles]; // window tiles [(tau - taub)][(i - ib)][j]
   int32_t ext[3][kMaxAxisTiles];    // extents per axis (t, h, w), global tile index
-  int16_t coff[3][kMaxAxisTiles];   // pool offset of the coefficients of e(k)
-  int32_t dist_e[3][kMaxDistinct];  // distinct clamped extents per axis ...
-  int32_t dist_off[3][kMaxDistinct];// ... and their pool offsets
-  int32_t n_dist[3];
   int32_t n_t, n_h, n_w;
   int32_t E[3], R[3];
   int32_t LT, LH, LW;               // full output extents
   int32_t taub, ib, ptr_nh;         // pointer-table origin and tile rows in it
   int32_t F0, nF, Y0, nY;           // output frame / row range of this window
-  int32_t Wv;                       // vectors per output row
-  int32_t plane0;                   // first (n, c) plane of this window
-  uint32_t total;                   // vectors in this window
-  FastDiv div_Wv, div_nY, div_nF, div_Rt, div_Rh, div_Rw;
-  int32_t pool_pairs;
+  int32_t plane0;                   // first (n, c) plane of this launch
+  int32_t rows_per_block;           // output rows per block
+  int32_t ew_max;                   // largest column blend extent (LDS table length)
+  FastDiv div_nF, div_Rt, div_Rh;
 };
 
 // ---------------------------------------------------------------------------
@@ -85,6 +79,6 @@ struct GNArgs {
 } // namespace sb
 
 // launchers (defined in the .hip files)
-hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, int grid, size_t lds,
+hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                            hipStream_t st);
 hipError_t sb_launch_groupnorm(const sb::GNArgs &a, int dtype, int vec16, hipStream_t st);

@@ -106,3 +106,49 @@ __device__ __forceinline__ Vec<VB> pack(const float *f) {
 }
 
 } // namespace sb
+
+namespace sb {
+
+// ---------------------------------------------------------------------------
+// Packed pairs of 16-bit storage values (two elements per 32-bit word)
+// ---------------------------------------------------------------------------
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// exact widening of a packed pair
+template <int DT> __device__ __forceinline__ f32x2 widen2(uint32_t w) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+  } else {
+    f32x2 r;
+    r.x = __uint_as_float(w << 16);
+    r.y = __uint_as_float(w & 0xFFFF0000u);
+    return r;
+  }
+}
+
+// both lanes rounded to nearest even with one conversion (v_cvt_pk_f16_f32 /
+// v_cvt_pk_bf16_f32)
+template <int DT> __device__ __forceinline__ uint32_t narrow2(f32x2 v) {
+  if constexpr (DT == DT_F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// RN_T(a + b) of two packed pairs.  For binary16 the addition is done in
+// binary16 (v_pk_add_f16), which equals rounding the exact sum to fp32 and
+// then to binary16 (fp32 has at least 2p + 2 bits, so the double rounding is
+// innocuous); for bfloat16 it is an fp32 add and one packed conversion.
+template <int DT> __device__ __forceinline__ uint32_t add2(uint32_t a, uint32_t b) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) + __builtin_bit_cast(f16x2, b));
+  } else {
+    const f32x2 fa = widen2<DT>(a), fb = widen2<DT>(b);
+    f32x2 s;
+    s.x = fa.x + fb.x;
+    s.y = fa.y + fb.y;
+    return narrow2<DT>(s);
+  }
+}
+
+} // namespace sb
