@@ -82,15 +82,16 @@ def main():
             for k, t in enumerate(tiles)]
     grid = [[[flat[(tau * nh + i) * nw + j] for j in range(nw)] for i in range(nh)] for tau in range(nt)]
     grid_arg = grid[0] if bw.ndim == 4 else grid
-    out = sb.vae_tile_blend_stitch(grid_arg, bw.blend, bw.row_limit)
+    # prepared calls: arguments are validated and marshalled once
+    blend = sb.BlendStitch(grid_arg, bw.blend, bw.row_limit)
+    out = blend.out
     blend_bytes = (bw.tile_elems() + out.numel()) * out.element_size()
     if has_gn:
         x = dev_t(x_np, gw.dtype)
         g = dev_t(g_np, gw.dtype)
         b = dev_t(b_np, gw.dtype)
-        y = torch.empty_like(x)
-        ws = torch.empty(sb.patch_groupnorm_workspace_bytes(tuple(x.shape), gw.groups, gw.split_axis,
-                                                            gw.n_patches), dtype=torch.uint8, device=dev)
+        gn = sb.PatchGroupNorm(x, gw.groups, gw.split_axis, gw.n_patches, gw.eps, g, b)
+        y = gn.out
         gn_bytes = 3 * x.numel() * x.element_size()
     else:
         gn_bytes = 0
@@ -99,12 +100,11 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        sb.vae_tile_blend_stitch(grid_arg, bw.blend, bw.row_limit, out=out)
+        blend()
         if ev is not None:
             ev[1].record()
         if has_gn:
-            sb.patch_groupnorm(x, gw.groups, gw.split_axis, gw.n_patches, gw.eps, g, b, out=y,
-                               workspace=ws)
+            gn()
             if ev is not None:
                 ev[2].record()
 

@@ -16,8 +16,9 @@ from typing import Optional, Sequence, Union
 
 import torch
 
-__all__ = ["vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents",
-           "patch_groupnorm", "patch_groupnorm_workspace_bytes", "SeamBlendError", "LIB_PATH"]
+__all__ = ["vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents", "BlendStitch",
+           "patch_groupnorm", "patch_groupnorm_workspace_bytes", "PatchGroupNorm",
+           "SeamBlendError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseamblend.so")
 if not os.path.exists(LIB_PATH):
@@ -129,43 +130,57 @@ def vae_tile_blend_stitch_output_extents(grid: Sequence[int], tile_extents: Sequ
     return tuple(out)
 
 
-def vae_tile_blend_stitch(tiles, blend_extent: Union[int, Sequence[int]],
-                          row_limit: Union[int, Sequence[int]],
-                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Blend, crop and stitch a grid of decoded tiles on the GPU.
+class BlendStitch:
+    """A prepared blend + crop + stitch call: validates the tile grid and builds
+    the C arguments once; each call enqueues the kernel on the current stream.
 
     tiles: ``tiles[i][j]`` 4-D ``[N,C,h_i,w_j]`` or ``tiles[tau][i][j]`` 5-D
     ``[N,C,t_tau,h_i,w_j]`` contiguous GPU tensors of one dtype (fp32, fp16,
-    bf16).  blend_extent / row_limit: int, (h, w) or (t, h, w).
-    Returns (or fills) the ``[N,C,(L_t,)L_h,L_w]`` output.
+    bf16).  blend_extent / row_limit: int, (h, w) or (t, h, w).  The call reads
+    the tiles' current contents, so the same object can be replayed after the
+    tiles are refilled (the tensors must stay alive and in place).
     """
-    ndim, grid3, flat, nt, nh, nw = _grid_of(tiles)
-    for k, t in enumerate(flat):
-        _require_gpu(t, f"tile {k}")
-    dtype, device = flat[0].dtype, flat[0].device
-    if any(t.dtype != dtype or t.device != device for t in flat):
-        raise ValueError("all tiles must share dtype and device")
-    N, C, et, eh, ew = _extents(grid3, ndim, nt, nh, nw)
-    E, R = _triple(blend_extent, "blend_extent"), _triple(row_limit, "row_limit")
-    if ndim == 4:
-        E, R = (0, E[1], E[2]), (1, R[1], R[2])
-    grid = (ndim, N, C, nt, nh, nw)
-    ext = list(et) + list(eh) + list(ew)
-    LT, LH, LW = vae_tile_blend_stitch_output_extents(grid, ext, E, R)
-    shape = (N, C, LH, LW) if ndim == 4 else (N, C, LT, LH, LW)
-    if out is None:
-        out = torch.empty(shape, dtype=dtype, device=device)
-    else:
-        _require_gpu(out, "out")
-        if tuple(out.shape) != shape or out.dtype != dtype or out.device != device:
-            raise ValueError(f"out must be {shape} {dtype} on {device}")
-    ptrs = (ctypes.c_void_p * len(flat))(*[t.data_ptr() for t in flat])
-    with torch.cuda.device(device):
-        rc = _lib.vae_tile_blend_stitch(ptrs, _arr(grid), _arr(ext), _arr(E), _arr(R), _DTYPE[dtype],
-                                        ctypes.c_void_p(out.data_ptr()),
-                                        ctypes.c_void_p(_stream_ptr(device)))
-    _check(rc, "vae_tile_blend_stitch")
-    return out
+
+    def __init__(self, tiles, blend_extent, row_limit, out: Optional[torch.Tensor] = None):
+        ndim, grid3, flat, nt, nh, nw = _grid_of(tiles)
+        for k, t in enumerate(flat):
+            _require_gpu(t, f"tile {k}")
+        dtype, device = flat[0].dtype, flat[0].device
+        if any(t.dtype != dtype or t.device != device for t in flat):
+            raise ValueError("all tiles must share dtype and device")
+        N, C, et, eh, ew = _extents(grid3, ndim, nt, nh, nw)
+        E, R = _triple(blend_extent, "blend_extent"), _triple(row_limit, "row_limit")
+        if ndim == 4:
+            E, R = (0, E[1], E[2]), (1, R[1], R[2])
+        grid = (ndim, N, C, nt, nh, nw)
+        ext = list(et) + list(eh) + list(ew)
+        LT, LH, LW = vae_tile_blend_stitch_output_extents(grid, ext, E, R)
+        shape = (N, C, LH, LW) if ndim == 4 else (N, C, LT, LH, LW)
+        if out is None:
+            out = torch.empty(shape, dtype=dtype, device=device)
+        else:
+            _require_gpu(out, "out")
+            if tuple(out.shape) != shape or out.dtype != dtype or out.device != device:
+                raise ValueError(f"out must be {shape} {dtype} on {device}")
+        self.out, self.device, self._tiles = out, device, flat
+        self._args = ((ctypes.c_void_p * len(flat))(*[t.data_ptr() for t in flat]), _arr(grid),
+                      _arr(ext), _arr(E), _arr(R), _DTYPE[dtype], ctypes.c_void_p(out.data_ptr()))
+
+    def __call__(self) -> torch.Tensor:
+        rc = _lib.vae_tile_blend_stitch(*self._args, ctypes.c_void_p(_stream_ptr(self.device)))
+        if rc != 0:
+            raise SeamBlendError(rc, "vae_tile_blend_stitch")
+        return self.out
+
+
+def vae_tile_blend_stitch(tiles, blend_extent: Union[int, Sequence[int]],
+                          row_limit: Union[int, Sequence[int]],
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Blend, crop and stitch a grid of decoded tiles on the GPU (see
+    BlendStitch).  Returns (or fills) the ``[N,C,(L_t,)L_h,L_w]`` output."""
+    plan = BlendStitch(tiles, blend_extent, row_limit, out)
+    with torch.cuda.device(plan.device):
+        return plan()
 
 
 def patch_groupnorm_workspace_bytes(shape: Sequence[int], groups: int, split_axis: int,
@@ -174,6 +189,58 @@ def patch_groupnorm_workspace_bytes(shape: Sequence[int], groups: int, split_axi
     if n == 0:
         raise SeamBlendError(-1, "patch_groupnorm_workspace_bytes")
     return int(n)
+
+
+class PatchGroupNorm:
+    """A prepared patch GroupNorm call over fixed x / out / gamma / beta
+    tensors (arguments validated and the workspace allocated once).  See
+    patch_groupnorm for the meaning of the arguments."""
+
+    def __init__(self, x: torch.Tensor, groups: int, split_axis: int, n_patches: int,
+                 eps: float = 1e-6, gamma: Optional[torch.Tensor] = None,
+                 beta: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None,
+                 patch_stats: Optional[torch.Tensor] = None):
+        _require_gpu(x, "x")
+        shape = tuple(x.shape)
+        dev = x.device
+        for name, t in (("gamma", gamma), ("beta", beta)):
+            if t is not None:
+                _require_gpu(t, name)
+                if t.dtype != x.dtype or t.numel() != shape[1] or t.device != dev:
+                    raise ValueError(f"{name} must be [C] of x's dtype on x's device")
+        if out is None:
+            out = torch.empty_like(x)
+        else:
+            _require_gpu(out, "out")
+            if tuple(out.shape) != shape or out.dtype != x.dtype or out.device != dev:
+                raise ValueError("out must match x")
+        need = patch_groupnorm_workspace_bytes(shape, groups, split_axis, n_patches)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        elif not workspace.is_cuda or workspace.device != dev:
+            raise ValueError("workspace must be a GPU tensor on x's device")
+        if patch_stats is not None:
+            if (patch_stats.dtype != torch.float32 or not patch_stats.is_cuda
+                    or not patch_stats.is_contiguous()
+                    or patch_stats.numel() != shape[0] * groups * n_patches * 3):
+                raise ValueError("patch_stats must be a contiguous float32 GPU tensor [N, G, P, 3]")
+        self.out, self.device = out, dev
+        self._keep = (x, gamma, beta, workspace, patch_stats)
+        self._args = (ctypes.c_void_p(x.data_ptr()), x.dim(), _arr(shape), groups, split_axis,
+                      n_patches, float(eps),
+                      ctypes.c_void_p(gamma.data_ptr() if gamma is not None else None),
+                      ctypes.c_void_p(beta.data_ptr() if beta is not None else None),
+                      _DTYPE[x.dtype], ctypes.c_void_p(out.data_ptr()),
+                      ctypes.c_void_p(workspace.data_ptr()),
+                      workspace.numel() * workspace.element_size(),
+                      ctypes.c_void_p(patch_stats.data_ptr() if patch_stats is not None else None))
+
+    def __call__(self) -> torch.Tensor:
+        rc = _lib.patch_groupnorm(*self._args, ctypes.c_void_p(_stream_ptr(self.device)))
+        if rc != 0:
+            raise SeamBlendError(rc, "patch_groupnorm")
+        return self.out
 
 
 def patch_groupnorm(x: torch.Tensor, groups: int, split_axis: int, n_patches: int,
@@ -187,37 +254,7 @@ def patch_groupnorm(x: torch.Tensor, groups: int, split_axis: int, n_patches: in
     ``patch_groupnorm_workspace_bytes`` bytes (allocated here if omitted).
     ``patch_stats``: optional float32 GPU tensor [N, G, P, 3] that receives
     per-patch (count, mean, M2)."""
-    _require_gpu(x, "x")
-    shape = tuple(x.shape)
-    dev = x.device
-    for name, t in (("gamma", gamma), ("beta", beta)):
-        if t is not None:
-            _require_gpu(t, name)
-            if t.dtype != x.dtype or t.numel() != shape[1] or t.device != dev:
-                raise ValueError(f"{name} must be [C] of x's dtype on x's device")
-    if out is None:
-        out = torch.empty_like(x)
-    else:
-        _require_gpu(out, "out")
-        if tuple(out.shape) != shape or out.dtype != x.dtype or out.device != dev:
-            raise ValueError("out must match x")
-    need = patch_groupnorm_workspace_bytes(shape, groups, split_axis, n_patches)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    elif not workspace.is_cuda or workspace.device != dev:
-        raise ValueError("workspace must be a GPU tensor on x's device")
-    if patch_stats is not None:
-        if (patch_stats.dtype != torch.float32 or not patch_stats.is_cuda or not patch_stats.is_contiguous()
-                or patch_stats.numel() != shape[0] * groups * n_patches * 3):
-            raise ValueError("patch_stats must be a contiguous float32 GPU tensor [N, G, P, 3]")
-    with torch.cuda.device(dev):
-        rc = _lib.patch_groupnorm(
-            ctypes.c_void_p(x.data_ptr()), x.dim(), _arr(shape), groups, split_axis, n_patches,
-            float(eps), ctypes.c_void_p(gamma.data_ptr() if gamma is not None else None),
-            ctypes.c_void_p(beta.data_ptr() if beta is not None else None), _DTYPE[x.dtype],
-            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
-            workspace.numel() * workspace.element_size(),
-            ctypes.c_void_p(patch_stats.data_ptr() if patch_stats is not None else None),
-            ctypes.c_void_p(_stream_ptr(dev)))
-    _check(rc, "patch_groupnorm")
-    return out
+    plan = PatchGroupNorm(x, groups, split_axis, n_patches, eps, gamma, beta, out, workspace,
+                          patch_stats)
+    with torch.cuda.device(plan.device):
+        return plan()

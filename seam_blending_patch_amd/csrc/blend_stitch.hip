@@ -51,6 +51,12 @@
 #ifndef SB_BLEND_NT
 #define SB_BLEND_NT 1 // nontemporal hints on tile loads (each tile element is read once)
 #endif
+#ifndef SB_BLEND_NT_STORE
+#define SB_BLEND_NT_STORE 0 // nontemporal hints on output stores (measured slower: L2 write-combining helps)
+#endif
+#ifndef SB_BLEND_THREADS
+#define SB_BLEND_THREADS 256
+#endif
 #ifndef SB_BLEND_LOADS
 #define SB_BLEND_LOADS 8 // 16-byte loads per lane in flight per batch
 #endif
@@ -170,7 +176,7 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
       if (!ok[k]) continue;
       char *dst = R.o + (int64_t)yy[k] * R.opitch + (int64_t)(xx[k] - R.x0) * EB;
       if constexpr (!HS && !WS && !TS) {
-        vstore<VB, true>(dst, m[k]);
+        vstore<VB, SB_BLEND_NT_STORE>(dst, m[k]);
       } else if constexpr (DT != DT_F32 && VB == 16) {
         // packed pairs of 16-bit elements
         constexpr int NW = Vec<VB>::NW;
@@ -219,7 +225,7 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
 #pragma unroll
           for (int w = 0; w < NW; ++w) S.w[w] = crossfade2<DT>(Sp.w[w], S.w[w], ta, tb);
         }
-        vstore<VB, true>(dst, S);
+        vstore<VB, SB_BLEND_NT_STORE>(dst, S);
       } else {
         float2 chh = make_float2(0.f, 0.f);
         if constexpr (HS) chh = R.ch[yy[k]];
@@ -265,14 +271,14 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
 #pragma unroll
           for (int e = 0; e < V; ++e) S[e] = crossfade<DT>(Sp[e], S[e], R.ct);
         }
-        vstore<VB, true>(dst, pack<DT, VB>(S));
+        vstore<VB, SB_BLEND_NT_STORE>(dst, pack<DT, VB>(S));
       }
     }
   }
 }
 
 template <int DT, int VB>
-__global__ __launch_bounds__(256) SB_BLEND_OCC void blend_stitch_kernel(const BlendArgs A) {
+__global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_kernel(const BlendArgs A) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
   extern __shared__ float2 s_tab[]; // [ew_max] column coefficients, then [rows_per_block] row ones
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(256) SB_BLEND_OCC void blend_stitch_kernel(const Bl
 hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                            hipStream_t st) {
   using namespace sb;
-  dim3 b(256);
+  dim3 b(SB_BLEND_THREADS);
   if (dtype == DT_F32) {
     if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_F32, 16>), grid, b, lds, st, a);
     else hipLaunchKernelGGL((blend_stitch_kernel<DT_F32, 4>), grid, b, lds, st, a);

@@ -27,6 +27,13 @@
 #include "sb_internal.h"
 #include "sb_vec.h"
 
+#ifndef SB_GN_NT_STORE
+#define SB_GN_NT_STORE 1 // nontemporal hints on y stores (measured faster here, unlike the blend)
+#endif
+#ifndef SB_GN_NT_LOAD2
+#define SB_GN_NT_LOAD2 1 // nontemporal hints on pass-2 loads of x (last use)
+#endif
+
 namespace sb {
 
 struct Stat {
@@ -53,6 +60,8 @@ __device__ __forceinline__ Stat shfl_down_stat(const Stat &s, int o) {
   t.m2 = __shfl_down(s.m2, o, 64);
   return t;
 }
+
+constexpr int kStatsBatch = 4; // vectors per thread whose loads are in flight together
 
 template <int DT, int VB>
 __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv div_big,
@@ -81,32 +90,40 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
   const char *gbase = (const char *)A.x +
                       (((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S + (int64_t)start * A.inner) * EB;
 
+  // Vectors q0 + tid + k * blockDim.x, in batches of kStatsBatch whose loads
+  // are issued together.  K (the shift) is the thread's first element.
   float K = 0.f, s1 = 0.f, s2 = 0.f, cnt = 0.f;
-  uint32_t q = q0 + tid;
-  if (q < q1) {
-    const uint32_t r = fdiv(q, dv);
-    const uint32_t pos = q - r * runv;
-    float f[V];
-    unpack<DT, VB>(vload<VB, false>(gbase + ((int64_t)r * row + (int64_t)pos * V) * EB), f);
-    K = f[0];
+  bool have = false;
+  for (uint32_t base = q0 + tid; base < q1; base += blockDim.x * kStatsBatch) {
+    Vec<VB> v[kStatsBatch];
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const float d = f[k] - K;
-      s1 += d;
-      s2 = fmaf(d, d, s2);
-    }
-    cnt = (float)V;
-    for (q += blockDim.x; q < q1; q += blockDim.x) {
-      const uint32_t r2 = fdiv(q, dv);
-      const uint32_t pos2 = q - r2 * runv;
-      unpack<DT, VB>(vload<VB, false>(gbase + ((int64_t)r2 * row + (int64_t)pos2 * V) * EB), f);
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        const float d = f[k] - K;
-        s1 += d;
-        s2 = fmaf(d, d, s2);
+    for (int u = 0; u < kStatsBatch; ++u) {
+      const uint32_t q = base + u * blockDim.x;
+      if (q < q1) {
+        const uint32_t r = fdiv(q, dv);
+        const uint32_t pos = q - r * runv;
+        v[u] = vload<VB, false>(gbase + ((int64_t)r * row + (int64_t)pos * V) * EB);
       }
-      cnt += (float)V;
+    }
+    if (!have) {
+      float f0[V];
+      unpack<DT, VB>(v[0], f0);
+      K = f0[0];
+      have = true;
+    }
+#pragma unroll
+    for (int u = 0; u < kStatsBatch; ++u) {
+      if (base + u * blockDim.x < q1) {
+        float f[V];
+        unpack<DT, VB>(v[u], f);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          const float d = f[k] - K;
+          s1 += d;
+          s2 = fmaf(d, d, s2);
+        }
+        cnt += (float)V;
+      }
     }
   }
   Stat st;
@@ -162,7 +179,7 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
 #pragma unroll
   for (int u = 0; u < kNormUnroll; ++u) {
     const int64_t q = q0 + (int64_t)u * blockDim.x + tid;
-    if (q < q1) xs[u] = vload<VB, true>(xb + q * V * EB);
+    if (q < q1) xs[u] = vload<VB, SB_GN_NT_LOAD2>(xb + q * V * EB);
   }
 
   // merge the group's partials: lane l holds (patch l / CPP, chunk l % CPP)
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
       unpack<DT, VB>(xs[u], f);
 #pragma unroll
       for (int k = 0; k < V; ++k) f[k] = fmaf(f[k] - mean, a, bet);
-      vstore<VB, true>(yb + q * V * EB, pack<DT, VB>(f));
+      vstore<VB, SB_GN_NT_STORE>(yb + q * V * EB, pack<DT, VB>(f));
     }
   }
 }
