@@ -130,13 +130,14 @@ def main():
     print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; blend {blend_avg_us:.1f} us "
           f"({blend_gbs:.0f} GB/s), groupnorm {gn_avg_us:.1f} us", file=sys.stderr, flush=True)
 
-    # optional: the same parts with the 256 MB last-level cache flushed first
+    # optional: the same parts with the 256 MB last-level cache flushed first by
+    # reading a 512 MB buffer (a read flush leaves no dirty lines to write back)
     flushed = None
     if args.flushed_reps > 0:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         fb, fg = [], []
         for _ in range(args.flushed_reps):
-            scratch.fill_(1)
+            scratch.sum()
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             step(e)
             torch.cuda.synchronize()
