@@ -120,16 +120,20 @@ size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape, int64_t g
  *   eps          added to the variance (fp32), >= 0.
  *   gamma, beta  device pointers to [C] of dtype, or NULL (1 and 0).
  *   out          device pointer like x; may be x itself (in place).
- *   workspace    device scratch of at least patch_groupnorm_workspace_bytes();
- *                caller-owned, contents need not be initialised.
+ *   workspace    device scratch of at least patch_groupnorm_workspace_bytes(),
+ *                16-byte aligned; caller-owned, contents need not be initialised.
  *   patch_stats  optional device pointer to N*G*P*3 floats, or NULL: receives
  *                per-patch (count, mean, M2), M2 = sum of squared deviations
- *                about the patch mean, merged in fp32 over that patch's chunks.
+ *                about the patch mean, merged in fp32 over that patch's chunks;
+ *                (0, 0, 0) for an empty patch.
  *   stream       hipStream_t or NULL.
  * Result: per (n, g), mean and M2 over the C/G channels and all spatial
  * positions, obtained by Chan-merging fp32 partial statistics in a fixed order
  * (chunks of a patch, then patches); var = M2 / count; rstd = 1/sqrt(var+eps);
  * y = (x - mean) * rstd * gamma_c + beta_c in fp32, rounded once to dtype.
+ * Statistics are taken about a shift K_g (the group's first element), so the
+ * mean is carried as K_g + m and x - mean is formed as (x - K_g) - m: inputs
+ * whose mean is large against their spread keep full fp32 accuracy.
  * Deterministic: the same inputs give the same bits on every call.
  */
 int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t groups,

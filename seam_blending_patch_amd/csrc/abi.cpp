@@ -348,7 +348,7 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
   while ((1 << a.log2CPP) < cpp) a.log2CPP++;
   a.per2 = 256 * 4; // vectors per pass-2 block (256 threads x 4)
   a.chunks2 = (int32_t)std::max<int64_t>(1, (S / V + a.per2 - 1) / a.per2);
-  P.ws_bytes = (size_t)shape[0] * groups * n_patches * cpp * 3 * sizeof(float);
+  P.ws_bytes = (size_t)shape[0] * groups * n_patches * cpp * 4 * sizeof(float); // (count, m, M2, K_g)
   if (P.ws_bytes == 0) P.ws_bytes = 16;
   return SB_OK;
 }
@@ -378,8 +378,8 @@ extern "C" int patch_groupnorm(const void *x, int ndim, const int64_t *shape, in
   if (workspace_bytes < P.ws_bytes)
     return fail(SB_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
                 P.ws_bytes);
-  if (!aligned(workspace, 4) || (patch_stats && !aligned(patch_stats, 4)))
-    return fail(SB_EARG, "workspace and patch_stats must be 4-byte aligned");
+  if (!aligned(workspace, 16) || (patch_stats && !aligned(patch_stats, 4)))
+    return fail(SB_EARG, "workspace must be 16-byte and patch_stats 4-byte aligned");
   const int EB = elem_bytes(dtype);
   if (!aligned(x, EB) || !aligned(out, EB) || (gamma && !aligned(gamma, EB)) || (beta && !aligned(beta, EB)))
     return fail(SB_EARG, "x, out, gamma and beta must be aligned to the element size");

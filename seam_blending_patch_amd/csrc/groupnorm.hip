@@ -7,21 +7,25 @@
 // GroupNorm -- global mean, variance = M2 / count (no Bessel correction).
 // Patches follow the Patchify split (first L mod P patches one longer).
 //
+// Every statistic is kept about a group shift K_g, the group's first element
+// (any data value of the group serves; it keeps fp32 deviations small when the
+// mean is large against the spread, so the mean is carried as K_g + m with a
+// small, accurately represented m, and x - mean is formed as (x - K_g) - m).
+//
 // Pass 1 (gn_stats_kernel): one block per (n, g, patch, chunk of the patch).
-//   Each thread accumulates a shifted sum and sum of squares about its first
-//   element (the shift keeps the fp32 sums well conditioned when the mean is
-//   large against the spread), turns them into (count, mean, M2), and the
-//   block merges those with Chan's pairwise formula
+//   Each thread accumulates the sum and sum of squares of x - K_g, turns
+//   them into (count, m, M2), and the block merges those with Chan's pairwise
+//   formula
 //       d = mu_B - mu_A, n = n_A + n_B, mu = mu_A + d n_B / n,
 //       M2 = M2_A + M2_B + d^2 n_A n_B / n
 //   first across the wavefront with shuffles, then across the 4 waves in LDS.
-//   One fp32 partial (count, mean, M2) per block goes to the workspace.
+//   One fp32 partial (count, m, M2, K_g) per block goes to the workspace.
 // Pass 2 (gn_norm_kernel): one block per (n, c) plane chunk.  Every wave
 //   issues its loads of x first, then merges the P x CPP partials of its group
 //   with a fixed shuffle tree (chunks of a patch first, then patches) -- the
 //   same order in every block, so results are deterministic -- and streams
-//   y = (x - mean) * (rstd * gamma_c) + beta_c back out with nontemporal
-//   stores.  Wave 0 of the first block of each group writes the optional
+//   y = ((x - K_g) - m) * (rstd * gamma_c) + beta_c back out with nontemporal
+//   stores.  K_g comes from the workspace, not from x, so out may alias x.  Wave 0 of the first block of each group writes the optional
 //   per-patch statistics.
 
 #include "sb_internal.h"
@@ -90,10 +94,12 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
   const char *gbase = (const char *)A.x +
                       (((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S + (int64_t)start * A.inner) * EB;
 
+  // the group shift K_g: the group's first element (a uniform scalar load)
+  const int64_t g0 = ((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S;
+  const float K = widen<DT>(DT == DT_F32 ? ((const uint32_t *)A.x)[g0] : ((const uint16_t *)A.x)[g0]);
   // Vectors q0 + tid + k * blockDim.x, in batches of kStatsBatch whose loads
-  // are issued together.  K (the shift) is the thread's first element.
-  float K = 0.f, s1 = 0.f, s2 = 0.f, cnt = 0.f;
-  bool have = false;
+  // are issued together.
+  float s1 = 0.f, s2 = 0.f, cnt = 0.f;
   for (uint32_t base = q0 + tid; base < q1; base += blockDim.x * kStatsBatch) {
     Vec<VB> v[kStatsBatch];
 #pragma unroll
@@ -104,12 +110,6 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
         const uint32_t pos = q - r * runv;
         v[u] = vload<VB, false>(gbase + ((int64_t)r * row + (int64_t)pos * V) * EB);
       }
-    }
-    if (!have) {
-      float f0[V];
-      unpack<DT, VB>(v[0], f0);
-      K = f0[0];
-      have = true;
     }
 #pragma unroll
     for (int u = 0; u < kStatsBatch; ++u) {
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
   Stat st;
   st.n = cnt;
   if (cnt > 0.f) {
-    const float m = s1 / cnt;
-    st.mean = K + m;
+    const float m = s1 / cnt; // mean of x - K_g
+    st.mean = m;
     st.m2 = fmaxf(s2 - s1 * m, 0.f);
   } else {
     st.mean = 0.f;
@@ -149,10 +149,8 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
   if (tid == 0) {
     Stat m = s_w[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = chan_merge(m, s_w[w]);
-    float *dst = A.part + (int64_t)b * 3;
-    dst[0] = m.n;
-    dst[1] = m.mean;
-    dst[2] = m.m2;
+    float4 *dst = reinterpret_cast<float4 *>(A.part) + b;
+    *dst = make_float4(m.n, m.mean, m.m2, K);
   }
 }
 
@@ -186,16 +184,19 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   const int lane = tid & 63;
   const int K = A.P * A.CPP;
   Stat st{0.f, 0.f, 0.f};
+  float kg = 0.f; // the group shift K_g (the same in every partial of the group)
   if (lane < K) {
-    const float *src = A.part + ((int64_t)(n * A.G + g) * K + lane) * 3;
-    st.n = src[0];
-    st.mean = src[1];
-    st.m2 = src[2];
+    const float4 src = reinterpret_cast<const float4 *>(A.part)[(int64_t)(n * A.G + g) * K + lane];
+    st.n = src.x;
+    st.mean = src.y;
+    st.m2 = src.z;
+    kg = src.w;
   }
+  const float Kg = __shfl(kg, 0, 64);
   const bool writer = A.patch_stats != nullptr && chunk == 0 && (ch % A.Cg) == 0 && tid < 64;
   if (writer && A.CPP == 1 && lane < A.P) {
     float *d = A.patch_stats + ((int64_t)(n * A.G + g) * A.P + lane) * 3;
-    d[0] = st.n; d[1] = st.mean; d[2] = st.m2;
+    d[0] = st.n; d[1] = st.n > 0.f ? Kg + st.mean : 0.f; d[2] = st.m2;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
     if ((lane & (2 * o - 1)) == 0 && lane + o < 64) st = chan_merge(st, t);
     if (writer && 2 * o == A.CPP && (lane & (A.CPP - 1)) == 0 && (lane >> A.log2CPP) < A.P) {
       float *d = A.patch_stats + ((int64_t)(n * A.G + g) * A.P + (lane >> A.log2CPP)) * 3;
-      d[0] = st.n; d[1] = st.mean; d[2] = st.m2;
+      d[0] = st.n; d[1] = st.n > 0.f ? Kg + st.mean : 0.f; d[2] = st.m2;
     }
   }
   const float cnt = __shfl(st.n, 0, 64);
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
       float f[V];
       unpack<DT, VB>(xs[u], f);
 #pragma unroll
-      for (int k = 0; k < V; ++k) f[k] = fmaf(f[k] - mean, a, bet);
+      for (int k = 0; k < V; ++k) f[k] = fmaf((f[k] - Kg) - mean, a, bet);
       vstore<VB, SB_GN_NT_STORE>(yb + q * V * EB, pack<DT, VB>(f));
     }
   }

@@ -61,7 +61,7 @@ struct GNArgs {
   void *out;
   const void *gamma;
   const void *beta;
-  float *part;        // partials [N][G][P][CPP][3]
+  float *part;        // partials [N][G][P][CPP][4]: count, mean of x - K_g, M2, K_g
   float *patch_stats; // optional [N][G][P][3]
   int32_t N, C, G, Cg;
   int64_t S;          // spatial elements per channel

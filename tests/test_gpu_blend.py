@@ -169,3 +169,39 @@ def test_rejects_bad_geometry_without_launching(sb):
     with pytest.raises(sb.SeamBlendError) as ei:
         sb.vae_tile_blend_stitch(grid, w.blend, w.row_limit)
     assert ei.value.code == -2
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_signed_zeros_subnormals_and_extremes(sb, dtype):
+    # tiles drawn from a value set with +-0, subnormal products and large
+    # magnitudes: rounding, sign of zero and subnormal handling must match
+    w = _wl(dtype, [48, 48, 24], [48, 48, 40], 16, 32, C=2, seed=9)
+    rng = np.random.default_rng(9)
+    specials = {
+        "fp32": [0.0, -0.0, 1e-38, -1e-38, 1.4e-45, 3e38, -3e38, 1.0, -0.5],
+        "fp16": [0.0, -0.0, 6e-8, -6e-8, 6.1e-5, -6.1e-5, 6.0e4, -6.0e4, 1.0, -0.5, 2.0 ** -20],
+        "bf16": [0.0, -0.0, 1e-38, -1e-38, 3e38, -3e38, 1.0, -0.5, 2.0 ** -130],
+    }[dtype]
+    tiles = []
+    for k in range(9):
+        shape = w.tile_shape(0, k // 3, k % 3)
+        v = rng.choice(np.array(specials, dtype=np.float64), size=shape)
+        mix = rng.random(shape) < 0.3
+        v = np.where(mix, rng.normal(0, 0.5, shape), v)
+        tiles.append(workloads.to_storage(v, dtype))
+    check(sb, w, tiles, "specials")
+
+
+def test_large_blend_extent(sb):
+    # e = 4096 columns: the largest coefficient table the kernel holds
+    w = _wl("fp16", [8], [4104, 4104], 4096, 8, C=1)
+    check(sb, w, workloads.draw_tiles(w), "e=4096")
+    w2 = _wl("bf16", [300, 300, 100], [320, 320], 200, 104, C=2)  # seam wider than the crop
+    check(sb, w2, workloads.draw_tiles(w2), "e=200")
+
+
+def test_sixty_four_tiles_per_axis(sb):
+    w = _wl("bf16", [24], [24] * 63 + [16], 8, 16, C=1)
+    check(sb, w, workloads.draw_tiles(w), "64 along W")
+    w2 = _wl("fp32", [24] * 63 + [9], [20], 8, 16, C=1)
+    check(sb, w2, workloads.draw_tiles(w2), "64 along H")

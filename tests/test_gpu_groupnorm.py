@@ -131,3 +131,19 @@ def test_workspace_too_small_is_rejected(sb):
     with pytest.raises(sb.SeamBlendError) as ei:
         sb.patch_groupnorm(x, 4, 2, 2, workspace=ws)
     assert ei.value.code == -3
+
+
+@pytest.mark.parametrize("dtype,offset", [("fp32", 1000.0), ("bf16", 300.0), ("fp16", 200.0)])
+def test_large_mean_against_spread(sb, dtype, offset):
+    # a mean far above the spread: the shifted sums and the Chan merges must
+    # not lose the variance to cancellation
+    gw = _gw((2, 16, 24, 40), dtype, 4, 3, 5, seed=21, offset=("fixed", [offset] * 5))
+    x, g, b = workloads.draw_groupnorm(gw)
+    check(sb, gw, x, g, b, f"offset {offset}")
+
+
+@pytest.mark.parametrize("G", [1, 48])
+def test_one_group_and_one_channel_per_group(sb, G):
+    gw = _gw((3, 48, 20, 12), "fp16", G, 2, 3, seed=22)
+    x, g, b = workloads.draw_groupnorm(gw)
+    check(sb, gw, x, g, b, f"G={G}")
