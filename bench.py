@@ -41,6 +41,8 @@ def parse():
                     help="extra per-part timings with a 512 MB cache flush before each (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling PMC byte counters)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of the step captured in a HIP graph")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
                     help="repeat the oracle step until this much CPU time has been measured")
     return ap.parse_args()
@@ -129,6 +131,22 @@ def main():
     gn_gbs = gn_bytes / (gn_avg_us * 1e-6) / 1e9 if has_gn else None
     print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; blend {blend_avg_us:.1f} us "
           f"({blend_gbs:.0f} GB/s), groupnorm {gn_avg_us:.1f} us", file=sys.stderr, flush=True)
+
+    # extra: the same step captured once in a HIP graph and replayed (three
+    # launches per replay); reported beside the main figure, not instead of it
+    graph_ms = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
 
     # optional: the same parts with the 256 MB last-level cache flushed first by
     # reading a 512 MB buffer (a read flush leaves no dirty lines to write back)
@@ -230,6 +248,8 @@ def main():
         "parts": {"blend": {"bytes": blend_bytes, "us": blend_avg_us, "GBps": blend_gbs},
                   "groupnorm": {"bytes": gn_bytes, "us": gn_avg_us, "GBps": gn_gbs}},
         "flushed": flushed,
+        "graph": None if graph_ms is None else {"ms_per_step": graph_ms,
+                                                 "value": total_bytes / (graph_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -65,7 +65,10 @@ __device__ __forceinline__ Stat shfl_down_stat(const Stat &s, int o) {
   return t;
 }
 
-constexpr int kStatsBatch = 4; // vectors per thread whose loads are in flight together
+#ifndef SB_GN_STATS_BATCH
+#define SB_GN_STATS_BATCH 4
+#endif
+constexpr int kStatsBatch = SB_GN_STATS_BATCH; // vectors per thread whose loads are in flight together
 
 template <int DT, int VB>
 __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv div_big,
