@@ -141,6 +141,47 @@ int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t group
                     const void *beta, int dtype, void *out, void *workspace,
                     size_t workspace_bytes, float *patch_stats, void *stream);
 
+/*
+ * Tile layout along one axis of a canvas of L latents (host only): writes the
+ * origin and extent of each tile and their count.  Defined by the unsloth
+ * Studio PR "size seam-free VAE tiles from measured peaks", sections "Problem"
+ * and "Change" and its commit log (stock tiles with edge slivers; 32-latent
+ * tiles with at least 16-latent overlaps spread evenly so the last ends at the
+ * edge at full size; a canvas within one tile is one tile; at a sliver, the
+ * fewest decoder calls, then the widest tile, decoding no more latents per
+ * side than the stock loop; the earlier fewest tiles of the smallest side).
+ *   rule / params:
+ *     SB_LAYOUT_STOCK          {T, S}: a tile of T at every multiple of S below L,
+ *                              the last cut short by the edge.
+ *     SB_LAYOUT_EDGE_ALIGNED   {t, ov}: the fewest tiles of side t whose neighbours
+ *                              overlap by >= ov, origin_k = floor(k (L - t) / (n - 1));
+ *                              one tile of L when L <= t.
+ *     SB_LAYOUT_FEWEST_CALLS   {T, S, ov, M}: the fewest tiles, then the widest side
+ *                              t <= M, with n * t <= B, the latents the stock (T, S) loop
+ *                              decodes along the axis, and overlaps >= ov; spread evenly.
+ *                              Up to rounding: when no whole side fits B but the exact
+ *                              covering does (L + (n - 1) ov <= B), the smallest covering
+ *                              side is taken.
+ *     SB_LAYOUT_SMALLEST_SIDE  {ov, M}: the fewest tiles of side <= M covering with
+ *                              overlaps >= ov, then the smallest such side; spread evenly.
+ *     SB_LAYOUT_AUTO           {T, S, floor_tile, floor_overlap}: the stock tiles when
+ *                              every one is >= floor_tile and every overlap >=
+ *                              floor_overlap, else EDGE_ALIGNED with
+ *                              t = max(floor_tile, T), ov = max(floor_overlap, T - S).
+ *   max_tiles: capacity of origins[] and extents[] (SB_EARG if exceeded).
+ * Returns 0, SB_EARG for bad parameters, SB_EGEOM if no layout satisfies the rule.
+ */
+typedef enum {
+  SB_LAYOUT_STOCK = 0,
+  SB_LAYOUT_EDGE_ALIGNED = 1,
+  SB_LAYOUT_FEWEST_CALLS = 2,
+  SB_LAYOUT_SMALLEST_SIDE = 3,
+  SB_LAYOUT_AUTO = 4
+} sb_layout_rule;
+
+int vae_tile_layout(int64_t L, int rule, const int64_t params[4], int64_t max_tiles,
+                    int64_t *origins, int64_t *extents, int64_t *n_tiles);
+
 /* Thread-local message describing the last non-zero return on this thread. */
 const char *seamblend_last_error(void);
 

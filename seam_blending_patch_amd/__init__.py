@@ -16,7 +16,7 @@ from typing import Optional, Sequence, Union
 
 import torch
 
-__all__ = ["vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents", "BlendStitch",
+__all__ = ["vae_tile_layout", "LAYOUT_RULES", "vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents", "BlendStitch",
            "patch_groupnorm", "patch_groupnorm_workspace_bytes", "PatchGroupNorm",
            "SeamBlendError", "LIB_PATH"]
 
@@ -40,6 +40,8 @@ _lib.patch_groupnorm.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64p, ctypes.c_
                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p, ctypes.c_void_p]
 _lib.patch_groupnorm.restype = ctypes.c_int
+_lib.vae_tile_layout.argtypes = [ctypes.c_int64, ctypes.c_int, _i64p, ctypes.c_int64, _i64p, _i64p, _i64p]
+_lib.vae_tile_layout.restype = ctypes.c_int
 _lib.seamblend_last_error.argtypes = []
 _lib.seamblend_last_error.restype = ctypes.c_char_p
 
@@ -118,6 +120,21 @@ def _extents(grid3, ndim, nt, nh, nw):
                 if tuple(t.shape) != want:
                     raise ValueError(f"tile ({tau},{i},{j}) has shape {tuple(t.shape)}, expected {want}")
     return N, C, et, eh, ew
+
+
+LAYOUT_RULES = {"stock": 0, "edge_aligned": 1, "fewest_calls": 2, "smallest_side": 3, "auto": 4}
+
+
+def vae_tile_layout(length: int, rule: str, params: Sequence[int], max_tiles: int = 4096):
+    """Tile layout along one axis (host-side): (origins, extents) lists.  Rules
+    and params as in ``include/seam_blend.h`` (``vae_tile_layout``)."""
+    p = list(params) + [0] * (4 - len(params))
+    o = (ctypes.c_int64 * max_tiles)()
+    e = (ctypes.c_int64 * max_tiles)()
+    n = ctypes.c_int64(0)
+    _check(_lib.vae_tile_layout(int(length), LAYOUT_RULES[rule], _arr(p), max_tiles, o, e,
+                                ctypes.byref(n)), "vae_tile_layout")
+    return list(o[: n.value]), list(e[: n.value])
 
 
 def vae_tile_blend_stitch_output_extents(grid: Sequence[int], tile_extents: Sequence[int],
