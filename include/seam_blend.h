@@ -142,6 +142,34 @@ int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t group
                     size_t workspace_bytes, float *patch_stats, void *stream);
 
 /*
+ * Normalised-ramp blend of wide tiles (unsloth Studio PR "size seam-free VAE
+ * tiles from measured peaks", the Qwen-Image-2.1 wide-tile commit, which
+ * the later commits extend to every image VAE and to the tiled encode).
+ * A tile has no weight within `margin` positions of an edge it shares with
+ * another tile (an edge inside the canvas) and ramps linearly to full weight
+ * over the next `ramp`: at whole distance d from such an edge the factor is
+ * clamp((d - margin) / ramp, 0, 1); a tile's weight along an axis is the
+ * product of its two edges' factors and its 2-D weight the product of its
+ * axes'.  Weights are normalised to 1 at every position; the sum of weight
+ * times value is accumulated in fp32 and rounded once to the storage type.
+ *   tiles:        n_h * n_w device pointers, raster order (i, j); tile (i, j) is a
+ *                 contiguous [N, C, (T,) h_i, w_j] array of dtype (frames are not tiled).
+ *   grid:         {ndim (4 | 5), N, C, 1, n_h, n_w}, n_h and n_w in 1..48.
+ *   tile_origins: 1 + n_h + n_w positions: 0 (frames), then the row origins, then the
+ *                 column origins; each axis starts at 0 and increases.
+ *   tile_extents: 1 + n_h + n_w extents: T (1 when ndim == 4), then h_i, then w_j.  The
+ *                 canvas along an axis ends where its last tile ends (< 2^20).
+ *   margin, ramp: per axis (t, h, w) in positions; [0] is ignored; margin >= 0, ramp >= 1.
+ *   out:          contiguous [N, C, (T,) L_h, L_w] of dtype; must not overlap a tile.
+ * Every position needs a tile with weight (overlaps wider than twice the margin),
+ * and at most 4 tiles may carry weight at one position of an axis: else SB_EGEOM.
+ * Enqueued on `stream`; allocates nothing; N * C == 0 is a no-op.
+ */
+int vae_tile_ramp_blend(const void *const *tiles, const int64_t grid[6], const int64_t *tile_origins,
+                        const int64_t *tile_extents, const int64_t margin[3], const int64_t ramp[3],
+                        int dtype, void *out, void *stream);
+
+/*
  * Tile layout along one axis of a canvas of L latents (host only): writes the
  * origin and extent of each tile and their count.  Defined by the unsloth
  * Studio PR "size seam-free VAE tiles from measured peaks", sections "Problem"

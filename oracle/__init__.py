@@ -15,6 +15,10 @@ Functions and the passages they follow:
 * ``groupnorm``     -- unsplit GroupNorm in double (DistVAE PR "Add tiled VAE
   parallelism & extended model support", PatchGroupNorm commit: equal
   nn.GroupNorm, global mean, divide by the count).
+* ``ramp_blend``, ``ramp_weight`` -- the normalised-ramp blend of wide tiles
+  in double (unsloth Studio PR "size seam-free VAE tiles from measured peaks",
+  the Qwen-Image-2.1 wide-tile commit: no weight within the margin of a shared
+  edge, a linear ramp over the next positions, weights normalised to 1).
 * ``patch_stats``, ``chan_merge`` -- per-patch (count, mean, M2) with the
   Patchify split (first ranks one band longer) and their Chan merge.
 
@@ -88,6 +92,14 @@ def lib():
         L.oracle_f16_to_f32.restype = ctypes.c_float
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_ramp_blend.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int64, i64p, i64p, i64p, i64p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_ramp_blend.restype = ctypes.c_int
+        L.oracle_ramp_weight.argtypes = [ctypes.c_int64] * 7
+        L.oracle_ramp_weight.restype = ctypes.c_double
         L.oracle_round_f32_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                              ctypes.c_void_p]
         L.oracle_round_f32_array.restype = None
@@ -142,6 +154,40 @@ def blend_workload(w, tiles):
     """``blend_stitch`` for a ``workloads.BlendWorkload``."""
     return blend_stitch(tiles, w.N, w.C, w.ext_t, w.ext_h, w.ext_w, w.blend, w.row_limit,
                         w.dtype, ndim=w.ndim)
+
+
+def ramp_weight(p, origin, extent, k, n, margin, ramp) -> float:
+    """Weight of tile k of n (origin, extent) at position p along one axis."""
+    return float(lib().oracle_ramp_weight(p, origin, extent, k, n, margin, ramp))
+
+
+def ramp_blend(tiles, lead_shape, origins_h, extents_h, origins_w, extents_w, margin, ramp,
+               dtype, with_magnitude=False):
+    """Normalised-ramp blend of wide tiles, in double.  ``tiles`` are
+    storage-form arrays of shape lead_shape + (extent_h_i, extent_w_j) in raster
+    order; ``margin`` and ``ramp`` are (H, W) pairs in positions.  Returns the
+    float64 output of shape lead_shape + (L_h, L_w) (and the weighted sum of
+    magnitudes when asked)."""
+    n_h, n_w = len(origins_h), len(origins_w)
+    assert len(tiles) == n_h * n_w
+    st = NP_STORAGE[dtype]
+    P = int(np.prod(lead_shape)) if len(lead_shape) else 1
+    keep = [np.ascontiguousarray(t, dtype=st) for t in tiles]
+    for k, t in enumerate(keep):
+        i, j = divmod(k, n_w)
+        assert t.size == P * extents_h[i] * extents_w[j], "tile size mismatch"
+    LH = max(o + e for o, e in zip(origins_h, extents_h))
+    LW = max(o + e for o, e in zip(origins_w, extents_w))
+    ptrs = (ctypes.c_void_p * len(keep))(*[t.ctypes.data for t in keep])
+    out = np.empty(tuple(lead_shape) + (LH, LW), dtype=np.float64)
+    mag = np.empty_like(out) if with_magnitude else None
+    rc = lib().oracle_ramp_blend(ptrs, P, n_h, n_w, _i64(origins_h), _i64(extents_h),
+                                 _i64(origins_w), _i64(extents_w), LH, LW, int(margin[0]),
+                                 int(ramp[0]), int(margin[1]), int(ramp[1]), DTYPE_CODE[dtype],
+                                 _ptr(out), None if mag is None else _ptr(mag))
+    if rc != 0:
+        raise ValueError(f"oracle_ramp_blend rejected the layout (rc={rc})")
+    return (out, mag) if with_magnitude else out
 
 
 def groupnorm(x, groups, eps, gamma, beta, dtype):

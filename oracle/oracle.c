@@ -36,6 +36,11 @@
  * (as already modified) into the current one along T, crop, and place.
  * The blend extent along an axis is clamped to both tiles' extents.
  *
+ * The normalised-ramp oracle ([P2], unsloth Studio PR "size seam-free VAE
+ * tiles from measured peaks", the Qwen-Image-2.1 wide-tile commit) sums, in
+ * double and one tile after another, each tile's value times its weight
+ * divided by the sum of all tiles' weights at that position.
+ *
  * The GroupNorm oracle is the plain definition of unsplit GroupNorm in
  * double: per (n, group) the mean over C/G channels and all spatial
  * positions, the variance as the mean squared deviation about that mean, and
@@ -422,6 +427,85 @@ void oracle_chan_merge(const double *stats, int64_t rows, int64_t P, double *mer
         }
         merged[r * 3 + 0] = n; merged[r * 3 + 1] = mean; merged[r * 3 + 2] = m2;
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* normalised-ramp blend of wide tiles                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * [P2] the Qwen-Image-2.1 wide-tile commit: a tile has no weight within the
+ * margin of an edge it shares with another tile (an edge inside the canvas),
+ * ramps linearly to full weight over the next `ramp` positions, and the
+ * weights are normalised to sum to 1 at every position; tiles are accumulated
+ * one after another into a wide accumulator.  Weight along one axis at
+ * position p of tile k (origin o, extent s, n tiles on the axis), with d the
+ * distance in whole positions from the shared edge:
+ *   lower edge shared (k > 0):     clamp((p - o - m) / r, 0, 1)
+ *   upper edge shared (k < n - 1): clamp((o + s - 1 - p - m) / r, 0, 1)
+ * the product of the two factors; the 2-D weight is the product of the axes'.
+ */
+static double clamp01(double v) { return v < 0.0 ? 0.0 : (v > 1.0 ? 1.0 : v); }
+
+double oracle_ramp_weight(int64_t p, int64_t o, int64_t s, int64_t k, int64_t n, int64_t m,
+                          int64_t r)
+{
+    if (p < o || p >= o + s) return 0.0;
+    double w = 1.0;
+    if (k > 0) w *= clamp01((double)(p - o - m) / (double)r);
+    if (k < n - 1) w *= clamp01((double)(o + s - 1 - p - m) / (double)r);
+    return w;
+}
+
+/*
+ * tiles:  n_h*n_w host pointers, raster order; tile (i,j) is a contiguous
+ *         [P, sh_i, sw_j] array of dtype (P = every leading dimension).
+ * oh, sh, ow, sw: tile origins and extents along H and W.
+ * out:    [P, LH, LW] doubles, the normalised weighted sum (not rounded).
+ * mag:    optional [P, LH, LW] doubles, the same sum over |value|.
+ * Returns 0, or -1 when a position has no tile with nonzero weight or an
+ * argument is out of range.
+ */
+int oracle_ramp_blend(const void *const *tiles, int64_t P, int64_t n_h, int64_t n_w,
+                      const int64_t *oh, const int64_t *sh, const int64_t *ow, const int64_t *sw,
+                      int64_t LH, int64_t LW, int64_t mh, int64_t rh, int64_t mw, int64_t rw,
+                      int dtype, double *out, double *mag)
+{
+    if (P < 0 || n_h < 1 || n_w < 1 || LH < 1 || LW < 1 || mh < 0 || mw < 0 || rh < 1 || rw < 1)
+        return -1;
+    for (int64_t i = 0; i < n_h; ++i) if (oh[i] < 0 || sh[i] < 1 || oh[i] + sh[i] > LH) return -1;
+    for (int64_t j = 0; j < n_w; ++j) if (ow[j] < 0 || sw[j] < 1 || ow[j] + sw[j] > LW) return -1;
+    /* the sum of the tiles' weights at every position */
+    double *wsum = calloc((size_t)(LH * LW), sizeof(double));
+    for (int64_t i = 0; i < n_h; ++i)
+        for (int64_t j = 0; j < n_w; ++j)
+            for (int64_t y = oh[i]; y < oh[i] + sh[i]; ++y)
+                for (int64_t x = ow[j]; x < ow[j] + sw[j]; ++x)
+                    wsum[y * LW + x] += oracle_ramp_weight(y, oh[i], sh[i], i, n_h, mh, rh) *
+                                        oracle_ramp_weight(x, ow[j], sw[j], j, n_w, mw, rw);
+    for (int64_t q = 0; q < LH * LW; ++q)
+        if (!(wsum[q] > 0.0)) { free(wsum); return -1; }
+    memset(out, 0, sizeof(double) * (size_t)(P * LH * LW));
+    if (mag) memset(mag, 0, sizeof(double) * (size_t)(P * LH * LW));
+    /* one tile after another, normalised weight times value into the accumulator */
+    for (int64_t i = 0; i < n_h; ++i)
+        for (int64_t j = 0; j < n_w; ++j) {
+            const void *src = tiles[i * n_w + j];
+            #pragma omp parallel for schedule(static)
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t y = 0; y < sh[i]; ++y)
+                    for (int64_t x = 0; x < sw[j]; ++x) {
+                        int64_t gy = oh[i] + y, gx = ow[j] + x;
+                        double w = oracle_ramp_weight(gy, oh[i], sh[i], i, n_h, mh, rh) *
+                                   oracle_ramp_weight(gx, ow[j], sw[j], j, n_w, mw, rw);
+                        if (w == 0.0) continue;
+                        double wn = w / wsum[gy * LW + gx];
+                        double v = (double)load_T(src, (p * sh[i] + y) * sw[j] + x, dtype);
+                        out[(p * LH + gy) * LW + gx] += wn * v;
+                        if (mag) mag[(p * LH + gy) * LW + gx] += wn * fabs(v);
+                    }
+        }
+    free(wsum);
+    return 0;
 }
 
 /* Batch forms of the storage conversions (used by the tests that pin the

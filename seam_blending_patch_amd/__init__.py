@@ -16,7 +16,7 @@ from typing import Optional, Sequence, Union
 
 import torch
 
-__all__ = ["vae_tile_layout", "LAYOUT_RULES", "vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents", "BlendStitch",
+__all__ = ["vae_tile_layout", "LAYOUT_RULES", "vae_tile_ramp_blend", "RampBlend", "vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents", "BlendStitch",
            "patch_groupnorm", "patch_groupnorm_workspace_bytes", "PatchGroupNorm",
            "SeamBlendError", "LIB_PATH"]
 
@@ -42,6 +42,9 @@ _lib.patch_groupnorm.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64p, ctypes.c_
 _lib.patch_groupnorm.restype = ctypes.c_int
 _lib.vae_tile_layout.argtypes = [ctypes.c_int64, ctypes.c_int, _i64p, ctypes.c_int64, _i64p, _i64p, _i64p]
 _lib.vae_tile_layout.restype = ctypes.c_int
+_lib.vae_tile_ramp_blend.argtypes = [ctypes.POINTER(ctypes.c_void_p), _i64p, _i64p, _i64p, _i64p, _i64p,
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+_lib.vae_tile_ramp_blend.restype = ctypes.c_int
 _lib.seamblend_last_error.argtypes = []
 _lib.seamblend_last_error.restype = ctypes.c_char_p
 
@@ -196,6 +199,81 @@ def vae_tile_blend_stitch(tiles, blend_extent: Union[int, Sequence[int]],
     """Blend, crop and stitch a grid of decoded tiles on the GPU (see
     BlendStitch).  Returns (or fills) the ``[N,C,(L_t,)L_h,L_w]`` output."""
     plan = BlendStitch(tiles, blend_extent, row_limit, out)
+    with torch.cuda.device(plan.device):
+        return plan()
+
+
+def _pair(v, name):
+    if isinstance(v, int):
+        return (int(v), int(v))
+    v = tuple(int(a) for a in v)
+    if len(v) != 2:
+        raise ValueError(f"{name} must be an int or (h, w)")
+    return v
+
+
+class RampBlend:
+    """A prepared normalised-ramp blend of wide tiles (``vae_tile_ramp_blend``).
+
+    tiles: ``tiles[i][j]`` contiguous GPU tensors ``[N,C,h_i,w_j]`` or
+    ``[N,C,T,h_i,w_j]`` (frames untiled) of one dtype.  origins_h / origins_w:
+    the tiles' row and column origins in positions.  margin / ramp: int or
+    (h, w), in positions (for decoded pixels: latents times the VAE's
+    compression ratio).  Each call enqueues the kernel on the current stream.
+    """
+
+    def __init__(self, tiles, origins_h: Sequence[int], origins_w: Sequence[int],
+                 margin: Union[int, Sequence[int]], ramp: Union[int, Sequence[int]],
+                 out: Optional[torch.Tensor] = None):
+        nh, nw = len(tiles), len(tiles[0])
+        if any(len(r) != nw for r in tiles):
+            raise ValueError("tile grid is ragged")
+        if len(origins_h) != nh or len(origins_w) != nw:
+            raise ValueError("one origin per tile row and per tile column")
+        flat = [t for row in tiles for t in row]
+        for k, t in enumerate(flat):
+            _require_gpu(t, f"tile {k}")
+        t0 = flat[0]
+        ndim, dtype, device = t0.dim(), t0.dtype, t0.device
+        if ndim not in (4, 5) or any(t.dim() != ndim or t.dtype != dtype or t.device != device for t in flat):
+            raise ValueError("tiles must all be 4-D or all 5-D, of one dtype and device")
+        lead = tuple(t0.shape[:-2])
+        eh = [tiles[i][0].shape[-2] for i in range(nh)]
+        ew = [tiles[0][j].shape[-1] for j in range(nw)]
+        for i in range(nh):
+            for j in range(nw):
+                if tuple(tiles[i][j].shape) != lead + (eh[i], ew[j]):
+                    raise ValueError(f"tile ({i},{j}) has shape {tuple(tiles[i][j].shape)}")
+        T = lead[2] if ndim == 5 else 1
+        LH = max(int(o) + e for o, e in zip(origins_h, eh))
+        LW = max(int(o) + e for o, e in zip(origins_w, ew))
+        shape = lead + (LH, LW)
+        if out is None:
+            out = torch.empty(shape, dtype=dtype, device=device)
+        else:
+            _require_gpu(out, "out")
+            if tuple(out.shape) != shape or out.dtype != dtype or out.device != device:
+                raise ValueError(f"out must be {shape} {dtype} on {device}")
+        m, r = _pair(margin, "margin"), _pair(ramp, "ramp")
+        grid = (ndim, lead[0], lead[1], 1, nh, nw)
+        self.out, self.device, self._tiles = out, device, flat
+        self._args = ((ctypes.c_void_p * len(flat))(*[t.data_ptr() for t in flat]), _arr(grid),
+                      _arr([0] + list(origins_h) + list(origins_w)), _arr([T] + eh + ew),
+                      _arr((0,) + m), _arr((0,) + r), _DTYPE[dtype], ctypes.c_void_p(out.data_ptr()))
+
+    def __call__(self) -> torch.Tensor:
+        rc = _lib.vae_tile_ramp_blend(*self._args, ctypes.c_void_p(_stream_ptr(self.device)))
+        if rc != 0:
+            raise SeamBlendError(rc, "vae_tile_ramp_blend")
+        return self.out
+
+
+def vae_tile_ramp_blend(tiles, origins_h: Sequence[int], origins_w: Sequence[int],
+                        margin: Union[int, Sequence[int]], ramp: Union[int, Sequence[int]],
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Normalised-ramp blend of a grid of wide tiles on the GPU (see RampBlend).
+    Returns (or fills) the ``[N,C,(T,)L_h,L_w]`` output."""
+    plan = RampBlend(tiles, origins_h, origins_w, margin, ramp, out)
     with torch.cuda.device(plan.device):
         return plan()
 

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libseamblend.so")
-SOURCES = ["abi.cpp", "layout.cpp", "blend_stitch.hip", "groupnorm.hip"]
+SOURCES = ["abi.cpp", "layout.cpp", "ramp.cpp", "blend_stitch.hip", "groupnorm.hip", "ramp_blend.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",

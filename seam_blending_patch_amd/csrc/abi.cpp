@@ -121,10 +121,12 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 extern "C" const char *seamblend_last_error(void) { return g_err.c_str(); }
 
-// error reporting for the other host files of the library (not exported)
+// error reporting and device properties for the other host files of the
+// library (not exported)
 extern "C" __attribute__((visibility("hidden"))) int sb_fail_message(int code, const char *msg) {
   return fail(code, "%s", msg);
 }
+extern "C" __attribute__((visibility("hidden"))) int sb_cu_count(void) { return cu_count(); }
 
 extern "C" int vae_tile_blend_stitch_output_extents(const int64_t grid[6], const int64_t *tile_extents,
                                                     const int64_t blend_extent[3],

@@ -76,9 +76,43 @@ struct GNArgs {
   int64_t per2;       // vectors per pass-2 block
 };
 
+// ---------------------------------------------------------------------------
+// normalised-ramp blend launch arguments
+// ---------------------------------------------------------------------------
+constexpr int kRampMaxAxisTiles = 48; // tiles per axis
+constexpr int kRampMaxCover = 4;      // tiles with weight at one position of an axis
+constexpr int kRampMaxChunks = 128;   // column chunks per launch
+constexpr int kRampMaxSegs = 32;      // row segments per launch
+constexpr int kRampMultiCols = 512;   // widest column chunk with several tiles (LDS weights)
+constexpr int kRampSingleVecs = 256;  // widest single-tile column chunk, in vectors
+constexpr int kRampPosBits = 20;      // positions along an axis < 2^20
+
+// A column chunk or row segment packs its first position (20 bits), its first
+// tile (6 bits) and its tile count minus one (2 bits); every tile from the
+// first to the last has weight somewhere in it and no other tile has any.
+__host__ __device__ constexpr uint32_t ramp_pack(uint32_t p0, uint32_t k0, uint32_t cnt) {
+  return p0 | (k0 << kRampPosBits) | ((cnt - 1) << 26);
+}
+
+struct RampArgs {
+  void *out;
+  const void *ptr[kMaxWindowTiles];      // tiles of rows [ib, ib + rows): ptr[(i - ib) * n_w + j]
+  int32_t oh[kRampMaxAxisTiles], sh[kRampMaxAxisTiles]; // H origins and extents
+  int32_t ow[kRampMaxAxisTiles], sw[kRampMaxAxisTiles]; // W origins and extents
+  uint32_t chunk[kRampMaxChunks + 1];    // packed column chunks; the entry after the last holds its end
+  uint32_t seg[kRampMaxSegs + 1];        // packed row segments; the entry after the last holds its end
+  int32_t band0[kRampMaxSegs + 1];       // first row band of each segment (prefix sums)
+  int32_t nseg, ib, n_h, n_w;
+  int32_t LH, LW, rows_pb;
+  int32_t mh, mw;                        // margins
+  float inv_rh, inv_rw;                  // 1 / ramp
+};
+
 } // namespace sb
 
 // launchers (defined in the .hip files)
 hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                            hipStream_t st);
 hipError_t sb_launch_groupnorm(const sb::GNArgs &a, int dtype, int vec16, hipStream_t st);
+hipError_t sb_launch_ramp(const sb::RampArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
+                          hipStream_t st);

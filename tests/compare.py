@@ -67,3 +67,19 @@ def groupnorm_check(got_f64: np.ndarray, ref_f64: np.ndarray, dtype: str):
         "n": int(d.size),
     }
     return (not bad.any()) and np.isfinite(got_f64).all(), rep
+
+
+def ramp_check(got_f64: np.ndarray, ref_f64: np.ndarray, mag_f64: np.ndarray, dtype: str):
+    """Normalised-ramp blend against the double oracle.  The kernel sums at
+    most 16 weighted terms in fp32 with weights carrying a few roundings each;
+    a bound of 2^-18 times the weighted sum of magnitudes covers that with
+    room, and a 16-bit output may then round to either neighbour of the exact
+    value: one step of the storage type on top.  Returns (ok, report)."""
+    d = np.abs(got_f64 - ref_f64)
+    tol = 2.0 ** -18 * mag_f64
+    if dtype != "fp32":
+        tol = tol + ulp(ref_f64, dtype)
+    bad = d > tol
+    rep = {"max_abs_err": float(d.max()) if d.size else 0.0, "n_out_of_tol": int(bad.sum()),
+           "n": int(d.size)}
+    return (not bad.any()) and bool(np.isfinite(got_f64).all()), rep

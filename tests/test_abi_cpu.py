@@ -123,3 +123,50 @@ def test_groupnorm_rejects_small_workspace_and_bad_args_on_host(sb):
     # empty tensors are a no-op that needs no workspace
     empty = (ctypes.c_int64 * 4)(0, 8, 16, 16)
     assert lib.patch_groupnorm(X, 4, empty, 4, 2, 2, 1e-6, None, None, 0, Y, None, 0, None, None) == 0
+
+
+def _ramp_call(lib, grid, origins, extents, margin=(0, 4, 4), ramp=(0, 8, 8), dtype=2, out=0x900000,
+               ptrs=None):
+    i64 = lambda v: (ctypes.c_int64 * len(v))(*v)  # noqa: E731
+    n = grid[4] * grid[5]
+    fake = ptrs if ptrs is not None else (ctypes.c_void_p * max(1, n))(*[0x100000 * (k + 1) for k in range(n)])
+    return lib.vae_tile_ramp_blend(fake, i64(grid), i64(origins), i64(extents), i64(margin), i64(ramp),
+                                   dtype, ctypes.c_void_p(out) if out else None, None)
+
+
+@pytest.mark.parametrize("grid,origins,extents,margin,ramp,dtype,code,needle", [
+    ((3, 1, 3, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32], (0, 4, 4), (0, 8, 8), 2, -1, "ndim"),
+    ((4, 1, 3, 2, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32], (0, 4, 4), (0, 8, 8), 2, -1, "frames"),
+    ((4, 1, 3, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32], (0, -1, 4), (0, 8, 8), 2, -1, "margin"),
+    ((4, 1, 3, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32], (0, 4, 4), (0, 8, 0), 2, -1, "ramp"),
+    ((4, 1, 3, 1, 1, 2), [0, 0, 0, 0], [1, 32, 32, 32], (0, 4, 4), (0, 8, 8), 2, -2, "increase"),
+    ((4, 1, 3, 1, 1, 2), [0, 0, 4, 16], [1, 32, 32, 32], (0, 4, 4), (0, 8, 8), 2, -2, "start at 0"),
+    ((4, 1, 3, 1, 1, 2), [0, 0, 0, 16], [1, 32, 40, 8], (0, 4, 4), (0, 8, 8), 2, -2, "ends past"),
+    ((4, 1, 3, 1, 1, 2), [0, 0, 0, 23], [1, 32, 32, 32], (0, 4, 4), (0, 8, 8), 2, -2, "no tile has weight"),
+    ((4, 1, 3, 1, 1, 5), [0, 0, 0, 2, 4, 6, 8], [1, 32] + [32] * 5, (0, 0, 0), (0, 8, 8), 2, -2, "at most"),
+    ((4, 1, 3, 1, 1, 49), [0, 0] + [k for k in range(49)], [1, 32] + [32] * 49, (0, 0, 0), (0, 8, 8), 2,
+     -1, "tiles per axis"),
+    ((4, 1, 3, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32], (0, 4, 4), (0, 8, 8), 7, -1, "dtype"),
+])
+def test_ramp_rejects_bad_layouts_on_host(sb, grid, origins, extents, margin, ramp, dtype, code, needle):
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    lib.vae_tile_ramp_blend.restype = ctypes.c_int
+    lib.seamblend_last_error.restype = ctypes.c_char_p
+    assert _ramp_call(lib, grid, origins, extents, margin, ramp, dtype) == code
+    assert needle.encode() in lib.seamblend_last_error()
+
+
+def test_ramp_rejects_bad_pointers_on_host(sb):
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    lib.vae_tile_ramp_blend.restype = ctypes.c_int
+    lib.seamblend_last_error.restype = ctypes.c_char_p
+    g, o, e = (4, 1, 3, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32]
+    assert _ramp_call(lib, g, o, e, out=0) == -1
+    nul = (ctypes.c_void_p * 2)(0x100000, 0)
+    assert _ramp_call(lib, g, o, e, ptrs=nul) == -1
+    mis = (ctypes.c_void_p * 2)(0x100001, 0x200000)
+    assert _ramp_call(lib, g, o, e, ptrs=mis) == -1
+    assert _ramp_call(lib, g, o, e, out=0x100010) == -1
+    assert b"overlaps" in lib.seamblend_last_error()
+    # an empty batch is a no-op before any pointer is looked at
+    assert _ramp_call(lib, (4, 0, 3, 1, 1, 2), o, e, out=0, ptrs=(ctypes.c_void_p * 2)(0, 0)) == 0

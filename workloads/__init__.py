@@ -296,3 +296,108 @@ def random_blend_workload(seed: int, dtype: str, ndim: int = 4, max_tiles: int =
     nw, ew, Ew, Rw = axis(max_tiles, max_ext, align)
     return BlendWorkload(f"random-{seed}-{dtype}-{ndim}d", dtype, ndim, N, C, et, eh, ew,
                          (Et, Eh, Ew), (Rt, Rh, Rw), seed=seed, std=std)
+
+
+# ----------------------------------------------------------------------------
+# wide tiles blended with the normalised ramp (decode in pixels, encode in
+# latents); origins and extents are stated as numbers, margins and ramps in
+# positions (latents times the VAE's compression ratio for decoded pixels)
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class RampWorkload:
+    name: str
+    dtype: str
+    lead: Sequence[int]        # (N, C) or (N, C, T)
+    origins_h: Sequence[int]
+    extents_h: Sequence[int]
+    origins_w: Sequence[int]
+    extents_w: Sequence[int]
+    margin: Sequence[int]      # (h, w)
+    ramp: Sequence[int]        # (h, w)
+    seed: int
+    std: float = 0.5
+    clamp: Optional[float] = 1.0
+
+    @property
+    def out_shape(self):
+        LH = max(o + e for o, e in zip(self.origins_h, self.extents_h))
+        LW = max(o + e for o, e in zip(self.origins_w, self.extents_w))
+        return tuple(self.lead) + (LH, LW)
+
+    def tile_shape(self, i: int, j: int):
+        return tuple(self.lead) + (self.extents_h[i], self.extents_w[j])
+
+
+def _scaled(latents: Sequence[int], ratio: int) -> List[int]:
+    return [int(v) * ratio for v in latents]
+
+
+# Qwen-Image-2.1 (16x): 2048 px = 128 latents in the 32-latent floor tiles with
+# 16-latent overlaps, spread evenly: origins 0, 16, ..., 96 latents.
+_Q21_2048 = list(range(0, 97, 16))
+# Qwen-Image-2.1 at 2752x1536 px: 172 x 96 latents, floor tiles spread evenly
+_Q21_2752_W = [0, 15, 31, 46, 62, 77, 93, 108, 124, 140]
+_Q21_1536_H = [0, 16, 32, 48, 64]
+
+RAMP_WORKLOADS = {
+    # decode, pixel space: margin 4 latents and ramp 8 latents times the ratio
+    "qwen21-2048-bf16": RampWorkload(
+        "qwen21-2048-bf16", "bf16", (1, 3), _scaled(_Q21_2048, 16), [512] * 7,
+        _scaled(_Q21_2048, 16), [512] * 7, (64, 64), (128, 128), seed=21),
+    "qwen21-2752x1536-bf16": RampWorkload(
+        "qwen21-2752x1536-bf16", "bf16", (1, 3, 1), _scaled(_Q21_1536_H, 16), [512] * 5,
+        _scaled(_Q21_2752_W, 16), [512] * 10, (64, 64), (128, 128), seed=22),
+    # FLUX.1 (8x) at 1600 px: two 120-latent tiles per side at 0 and 80 latents
+    "flux-1600-bf16": RampWorkload(
+        "flux-1600-bf16", "bf16", (1, 3), [0, 640], [960, 960], [0, 640], [960, 960],
+        (32, 32), (64, 64), seed=23),
+    # encode, latent space: 64-latent tiles with 32-latent overlaps, the
+    # decode's margin and ramp in latents; 16 latent channels; a 2048 px
+    # reference at 16x is 128 latents
+    "qwen21-encode-2048-bf16": RampWorkload(
+        "qwen21-encode-2048-bf16", "bf16", (1, 16), [0, 32, 64], [64] * 3, [0, 32, 64], [64] * 3,
+        (4, 4), (8, 8), seed=24, std=1.0, clamp=None),
+}
+
+
+def draw_ramp_tiles(w: RampWorkload, rng: Optional[np.random.Generator] = None):
+    """Tiles in raster order (i, j); each N(0, std), optionally clamped."""
+    rng = rng if rng is not None else np.random.default_rng(w.seed)
+    out = []
+    for i in range(len(w.origins_h)):
+        for j in range(len(w.origins_w)):
+            v = rng.normal(0.0, w.std, size=w.tile_shape(i, j))
+            if w.clamp is not None:
+                np.clip(v, -w.clamp, w.clamp, out=v)
+            out.append(to_storage(v, w.dtype))
+    return out
+
+
+def random_ramp_workload(seed: int, dtype: str, lead=(1, 2), max_tiles: int = 4, max_ext: int = 48,
+                         align: int = 1) -> RampWorkload:
+    """Random increasing origins and extents with every tile inside the canvas,
+    overlaps wide enough for a tile with weight everywhere (more than twice the
+    margin plus one), and `align` dividing every W origin and extent."""
+    rng = np.random.default_rng(seed)
+
+    def axis(a):
+        m = int(rng.integers(0, 5))
+        r = int(rng.integers(1, 9))
+        n = int(rng.integers(1, max_tiles + 1))
+        s = max(2 * m + 2 + a, int(rng.integers(2 * m + 2, max_ext + 1)))
+        s = -(-s // a) * a
+        origins, extents = [0], [s]
+        for k in range(1, n):
+            ov_min = 2 * m + 2
+            stride = int(rng.integers(1, max(2, s - ov_min + 1)))
+            stride = max(a, stride // a * a)
+            if s - stride < ov_min:
+                break
+            origins.append(origins[-1] + stride)
+            extents.append(s)
+        return origins, extents, m, r
+
+    oh, eh, mh, rh = axis(1)
+    ow, ew, mw, rw = axis(align)
+    return RampWorkload(f"ramp-random-{seed}-{dtype}", dtype, tuple(lead), oh, eh, ow, ew,
+                        (mh, mw), (rh, rw), seed=seed, clamp=None)
