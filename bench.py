@@ -45,7 +45,65 @@ def parse():
                     help="skip the extra timing of the step captured in a HIP graph")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
                     help="repeat the oracle step until this much CPU time has been measured")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra rows (normalised-ramp wide-tile blend, tiled-encode blends)")
     return ap.parse_args()
+
+
+def ramp_bytes(w, elem):
+    """Algorithmic bytes of one normalised-ramp blend: every tile position with
+    weight read once (a tile weighs nothing within the margin of a shared edge,
+    so those positions are never needed) and every output position written once."""
+    def counts(origins, extents, m):
+        n, c = len(origins), []
+        for k, (o, e) in enumerate(zip(origins, extents)):
+            lo = o + m + 1 if k > 0 else o
+            hi = o + e - 1 - m if k < n - 1 else o + e
+            c.append(max(0, hi - lo))
+        return c
+    ch = counts(w.origins_h, w.extents_h, w.margin[0])
+    cw = counts(w.origins_w, w.extents_w, w.margin[1])
+    planes = 1
+    for v in w.lead:
+        planes *= v
+    LH, LW = w.out_shape[-2:]
+    return planes * (sum(ch) * sum(cw) + LH * LW) * elem
+
+
+def time_launches(torch, call, nbytes, steps, warmup, flushed_reps, dev):
+    """Average launch time with HIP events on the current stream (the launches
+    queued behind a short device-side wait, so the host's per-call cost is not
+    inside the timed intervals), and the median over `flushed_reps` launches
+    each after a 512 MB read flush."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda._sleep(20_000_000)
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / steps
+    row = {"bytes": nbytes, "us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+           "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    if flushed_reps > 0:
+        import numpy as np
+        scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        f = []
+        for _ in range(flushed_reps):
+            scratch.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            f.append(a.elapsed_time(b))
+        del scratch
+        med = float(np.median(f)) * 1e3
+        row.update({"flushed_us_median": med, "flushed_GBps": nbytes / (med * 1e-6) / 1e9})
+    return row
 
 
 def main():
@@ -177,15 +235,56 @@ def main():
         torch.cuda.synchronize()
         del src_c, dst_c
 
-    # traffic from committed PMC counters, only while the kernel source is unchanged
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "blend_traffic.json")
-    src = os.path.join(ROOT, "seam_blending_patch_amd", "csrc", "blend_stitch.hip")
+    # extra rows: the normalised-ramp blend of wide tiles (decode, pixel space;
+    # encode, latent space) and the stock blend on tiled-encode latents; each
+    # timed on its own, outside the step and its figure
+    extra = None
+    if not args.no_extra:
+        extra = {}
+        for name in ("qwen21-2048-bf16", "qwen21-2752x1536-bf16", "flux-1600-bf16", "qwen21-encode-2048-bf16"):
+            rw = workloads.RAMP_WORKLOADS[name]
+            rt = workloads.draw_ramp_tiles(rw)
+            nw_ = len(rw.origins_w)
+            rgrid = [[dev_t(rt[i * nw_ + j], rw.dtype).reshape(rw.tile_shape(i, j)) for j in range(nw_)]
+                     for i in range(len(rw.origins_h))]
+            call = sb.RampBlend(rgrid, rw.origins_h, rw.origins_w, rw.margin, rw.ramp)
+            row = time_launches(torch, call, ramp_bytes(rw, call.out.element_size()), args.steps,
+                                args.warmup, args.flushed_reps, dev)
+            row.update({"kernel": "ramp_blend_kernel", "out_shape": list(rw.out_shape),
+                        "tiles": [len(rw.origins_h), len(rw.origins_w)]})
+            extra["ramp:" + name] = row
+            del rgrid, call
+        for name, ew in workloads.ENCODE_BLEND_WORKLOADS.items():
+            et = workloads.draw_tiles(ew)
+            ent, enh, enw = ew.grid
+            eflat = [dev_t(t, ew.dtype).reshape(ew.tile_shape(0, k // enw, k % enw)) for k, t in enumerate(et)]
+            call = sb.BlendStitch([[eflat[i * enw + j] for j in range(enw)] for i in range(enh)], ew.blend,
+                                  ew.row_limit)
+            nbytes = (ew.tile_elems() + call.out.numel()) * call.out.element_size()
+            row = time_launches(torch, call, nbytes, args.steps, args.warmup, args.flushed_reps, dev)
+            row.update({"kernel": "blend_stitch_kernel", "out_shape": list(call.out.shape)})
+            extra["encode-blend:" + name] = row
+            del eflat, call
+        torch.cuda.synchronize()
+        for k, r in extra.items():
+            print(f"# extra {k}: {r['us']:.1f} us, {r['GBps']:.0f} GB/s ({100 * r['frac']:.0f}% of peak)",
+                  file=sys.stderr, flush=True)
+
+    # HBM traffic per launch from the committed PMC counters, reported only
+    # while the sources they were taken on are unchanged
+    traffic_rec = {}
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
-        rec = json.load(open(tpath))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("kernel_sha256") == sha and rec.get("config") == args.config:
-            traffic = rec.get("hbm_bytes_per_launch")
+        for name, rec_t in json.load(open(tpath)).get("launches", {}).items():
+            same = all(os.path.exists(os.path.join(ROOT, f)) and
+                       hashlib.sha256(open(os.path.join(ROOT, f), "rb").read()).hexdigest() == h
+                       for f, h in rec_t["sources_sha256"].items())
+            if same:
+                traffic_rec[name] = rec_t["hbm_bytes_per_launch"]
+    traffic = traffic_rec.get(f"config{args.config}-blend")
+    if extra:
+        for k, r in extra.items():
+            r["traffic"] = traffic_rec.get(k)
 
     # parity of this run's output and the CPU baseline (the oracle on all host cores)
     import oracle
@@ -252,6 +351,7 @@ def main():
                                                  "value": total_bytes / (graph_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,
         "parity": parity,
+        "extra": extra,
     }
     print(json.dumps(rec), flush=True)
 

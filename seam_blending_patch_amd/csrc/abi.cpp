@@ -223,8 +223,15 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   }
   const int cus = cu_count();
   const int64_t total_vec = planes * At.L * Ah.L * (Aw.L / V);
-  const int64_t per_block =
-      std::min<int64_t>(8192, std::max<int64_t>(1024, total_vec / ((int64_t)cus * SB_BLEND_BLOCKS_PER_CU)));
+#ifndef SB_BLEND_PER_BLOCK_MIN
+#define SB_BLEND_PER_BLOCK_MIN 1024
+#endif
+#ifndef SB_BLEND_PER_BLOCK_MAX
+#define SB_BLEND_PER_BLOCK_MAX 8192
+#endif
+  const int64_t per_block = std::min<int64_t>(
+      SB_BLEND_PER_BLOCK_MAX,
+      std::max<int64_t>(SB_BLEND_PER_BLOCK_MIN, total_vec / ((int64_t)cus * SB_BLEND_BLOCKS_PER_CU)));
   int64_t rows_pb = std::max<int64_t>(1, std::min<int64_t>(1024, per_block / seg_max));
   rows_pb = std::min<int64_t>(rows_pb, Ah.L);
   {

@@ -223,26 +223,37 @@ extern "C" int vae_tile_ramp_blend(const void *const *tiles, const int64_t grid[
   sb::RampArgs A;
   std::memset(&A, 0, sizeof A);
   A.out = out;
-  for (int64_t i = 0; i < n_h; ++i) { A.oh[i] = (int32_t)H.o[i]; A.sh[i] = (int32_t)H.s[i]; }
-  for (int64_t j = 0; j < n_w; ++j) { A.ow[j] = (int32_t)W.o[j]; A.sw[j] = (int32_t)W.s[j]; }
-  A.n_h = (int32_t)n_h;
-  A.n_w = (int32_t)n_w;
-  A.LH = (int32_t)H.L;
-  A.LW = (int32_t)W.L;
-  A.mh = (int32_t)H.m;
-  A.mw = (int32_t)W.m;
-  A.inv_rh = 1.0f / (float)H.r;
-  A.inv_rw = 1.0f / (float)W.r;
+  for (int64_t i = 0; i < n_h; ++i) { A.t.oh[i] = (int32_t)H.o[i]; A.t.sh[i] = (int32_t)H.s[i]; }
+  for (int64_t j = 0; j < n_w; ++j) { A.t.ow[j] = (int32_t)W.o[j]; A.t.sw[j] = (int32_t)W.s[j]; }
+  A.t.n_h = (int32_t)n_h;
+  A.t.n_w = (int32_t)n_w;
+  A.t.LH = (int32_t)H.L;
+  A.t.LW = (int32_t)W.L;
+  A.t.mh = (int32_t)H.m;
+  A.t.mw = (int32_t)W.m;
+  A.t.inv_rh = 1.0f / (float)H.r;
+  A.t.inv_rw = 1.0f / (float)W.r;
 
-  // Rows per block: about total / (cus * 8) vectors per block, clamped to
-  // [1024, 8192], over the average chunk width.
+  // Rows per block: about total / (cus * SB_RAMP_BLOCKS_PER_CU) vectors per
+  // block, clamped to [SB_RAMP_PER_BLOCK_MIN, SB_RAMP_PER_BLOCK_MAX], over the
+  // average chunk width.
+#ifndef SB_RAMP_BLOCKS_PER_CU
+#define SB_RAMP_BLOCKS_PER_CU 8
+#endif
+#ifndef SB_RAMP_PER_BLOCK_MIN
+#define SB_RAMP_PER_BLOCK_MIN 512
+#endif
+#ifndef SB_RAMP_PER_BLOCK_MAX
+#define SB_RAMP_PER_BLOCK_MAX 8192
+#endif
   const int64_t total_vec = planes * H.L * (W.L / V);
-  const int64_t per_block =
-      std::min<int64_t>(8192, std::max<int64_t>(1024, total_vec / ((int64_t)sb_cu_count() * 8)));
+  const int64_t per_block = std::min<int64_t>(
+      SB_RAMP_PER_BLOCK_MAX,
+      std::max<int64_t>(SB_RAMP_PER_BLOCK_MIN, total_vec / ((int64_t)sb_cu_count() * SB_RAMP_BLOCKS_PER_CU)));
   const int64_t avg_chunk = std::max<int64_t>(1, (W.L / V) / (int64_t)chunks.size());
   int64_t rows_pb = std::max<int64_t>(1, std::min<int64_t>(1024, per_block / avg_chunk));
   rows_pb = std::max(std::min(rows_pb, H.L), (H.L + 59999) / 60000); // row bands fit grid.z
-  A.rows_pb = (int32_t)rows_pb;
+  A.t.rows_pb = (int32_t)rows_pb;
 
   bool multi_w = false, multi_h = false;
   int64_t multi_cols = 0;
@@ -270,24 +281,24 @@ extern "C" int vae_tile_ramp_blend(const void *const *tiles, const int64_t grid[
     }
     if (s1 == s0)
       return failf(SB_EGEOM, "%lld tiles per row: a row segment exceeds one launch window", (long long)n_w);
-    A.ib = imin;
+    A.t.ib = imin;
     for (int k = 0; k < sb::kMaxWindowTiles; ++k) A.ptr[k] = nullptr;
     for (int i = imin; i < imax; ++i)
       for (int64_t j = 0; j < n_w; ++j) A.ptr[(i - imin) * n_w + j] = tiles[i * n_w + j];
-    A.nseg = (int32_t)(s1 - s0);
+    A.t.nseg = (int32_t)(s1 - s0);
     int32_t b0 = 0;
     for (size_t s = s0; s < s1; ++s) {
-      A.seg[s - s0] = sb::ramp_pack((uint32_t)hr[s].p0, (uint32_t)hr[s].k0, (uint32_t)hr[s].cnt);
-      A.band0[s - s0] = b0;
+      A.t.seg[s - s0] = sb::ramp_pack((uint32_t)hr[s].p0, (uint32_t)hr[s].k0, (uint32_t)hr[s].cnt);
+      A.t.band0[s - s0] = b0;
       b0 += (int32_t)((hr[s].p1 - hr[s].p0 + rows_pb - 1) / rows_pb);
     }
-    A.seg[s1 - s0] = sb::ramp_pack((uint32_t)hr[s1 - 1].p1, 0, 1);
-    A.band0[s1 - s0] = b0;
+    A.t.seg[s1 - s0] = sb::ramp_pack((uint32_t)hr[s1 - 1].p1, 0, 1);
+    A.t.band0[s1 - s0] = b0;
     for (size_t c0 = 0; c0 < chunks.size(); c0 += sb::kRampMaxChunks) {
       const size_t c1 = std::min(chunks.size(), c0 + (size_t)sb::kRampMaxChunks);
       for (size_t c = c0; c < c1; ++c)
-        A.chunk[c - c0] = sb::ramp_pack((uint32_t)chunks[c].p0, (uint32_t)chunks[c].k0, (uint32_t)chunks[c].cnt);
-      A.chunk[c1 - c0] = sb::ramp_pack((uint32_t)chunks[c1 - 1].p1, 0, 1);
+        A.t.chunk[c - c0] = sb::ramp_pack((uint32_t)chunks[c].p0, (uint32_t)chunks[c].k0, (uint32_t)chunks[c].cnt);
+      A.t.chunk[c1 - c0] = sb::ramp_pack((uint32_t)chunks[c1 - 1].p1, 0, 1);
       const dim3 g((unsigned)planes, (unsigned)(c1 - c0), (unsigned)b0);
       hipError_t e = sb_launch_ramp(A, dtype, vec16 ? 1 : 0, g, lds, st);
       if (e != hipSuccess) return failf(SB_ELAUNCH, "ramp blend launch failed: %s", hipGetErrorString(e));

@@ -28,7 +28,7 @@
 #define SB_RAMP_THREADS 256
 #endif
 #ifndef SB_RAMP_BATCH
-#define SB_RAMP_BATCH 4 // items whose loads are issued together
+#define SB_RAMP_BATCH 1 // items whose loads are issued together (more costs occupancy; measured best)
 #endif
 
 namespace sb {
@@ -61,6 +61,15 @@ __device__ __forceinline__ void normalised_weights(int p, int k0, int cnt, int n
 #pragma unroll
   for (int k = 0; k < kRampMaxCover; ++k)
     if (k < cnt) t[k * stride] = w[k] / sum;
+}
+
+// values the whole block shares, read from LDS: held in scalar registers
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const char *uniform(const char *p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const char *)(((uint64_t)hi << 32) | lo);
 }
 
 struct Block {
@@ -156,20 +165,23 @@ __device__ __forceinline__ void run_items(const Block &B, int nh, int nw) {
                           pack<DT, VB>(acc));
       }
     } else {
-      // general case: up to 4 x 4 tiles, one item at a time
+      // general case: up to 4 x 4 tiles, one item at a time (the loops are
+      // unrolled to the maximum so the tile table stays in registers)
 #pragma unroll 1
       for (int u = 0; u < U; ++u) {
         if (!live[u]) continue;
         float acc[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[e] = 0.0f;
-#pragma unroll 1
-        for (int j = 0; j < nw; ++j) {
+#pragma unroll
+        for (int j = 0; j < kRampMaxCover; ++j) {
+          if (j >= nw) break;
           float col[V];
 #pragma unroll
           for (int e = 0; e < V; ++e) col[e] = 0.0f;
-#pragma unroll 1
-          for (int i = 0; i < nh; ++i) {
+#pragma unroll
+          for (int i = 0; i < kRampMaxCover; ++i) {
+            if (i >= nh) break;
             const float hw = nh == 1 ? 1.0f : B.wh[i * B.rows + ir[u]];
             float f[V];
             unpack<DT, VB>(vload<VB, true>(B.tile[i][j] + ((int64_t)(B.y0 + ir[u]) * B.tw[j] + B.x0 + ic[u] * V) * EB), f);
@@ -190,32 +202,44 @@ __device__ __forceinline__ void run_items(const Block &B, int nh, int nw) {
 template <int DT, int VB>
 __global__ __launch_bounds__(SB_RAMP_THREADS) void ramp_blend_kernel(const RampArgs A) {
   extern __shared__ float lds[];
+  __shared__ RampTables T;
   constexpr int EB = Elem<DT>::bytes;
   const int64_t plane = blockIdx.x;
   const int c = blockIdx.y;
   const int band = blockIdx.z;
   constexpr uint32_t PM = (1u << kRampPosBits) - 1u;
 
+  // the decode tables, copied to LDS in one cooperative load
+  {
+    constexpr int n16 = (int)(sizeof(RampTables) / 16);
+    const uint4 *src = reinterpret_cast<const uint4 *>(&A.t);
+    uint4 *dst = reinterpret_cast<uint4 *>(&T);
+    for (int q = threadIdx.x; q < n16; q += SB_RAMP_THREADS) dst[q] = src[q];
+  }
+  __syncthreads();
+
   // column chunk
-  const uint32_t cp = A.chunk[c];
+  const uint32_t cp = (uint32_t)uniform((int)T.chunk[c]);
   const int x0 = (int)(cp & PM), j0 = (int)((cp >> kRampPosBits) & 63u), nw = (int)(cp >> 26) + 1;
-  const int x1 = (int)(A.chunk[c + 1] & PM);
+  const int x1 = uniform((int)(T.chunk[c + 1] & PM));
   // row segment holding this band (the last with band0 <= band)
+  const int nseg = uniform(T.nseg);
   int s = 0;
-  while (s + 1 < A.nseg && A.band0[s + 1] <= band) ++s;
-  const uint32_t sp = A.seg[s];
+  while (s + 1 < nseg && uniform(T.band0[s + 1]) <= band) ++s;
+  const uint32_t sp = (uint32_t)uniform((int)T.seg[s]);
   const int sy0 = (int)(sp & PM), i0 = (int)((sp >> kRampPosBits) & 63u), nh = (int)(sp >> 26) + 1;
-  const int sy1 = (int)(A.seg[s + 1] & PM);
-  const int y0 = sy0 + (band - A.band0[s]) * A.rows_pb;
-  const int y1 = min(y0 + A.rows_pb, sy1);
+  const int sy1 = uniform((int)(T.seg[s + 1] & PM));
+  const int rows_pb = uniform(T.rows_pb);
+  const int y0 = sy0 + (band - uniform(T.band0[s])) * rows_pb;
+  const int y1 = min(y0 + rows_pb, sy1);
 
   Block B;
-  B.LW = A.LW;
+  B.LW = uniform(T.LW);
   B.x0 = x0;
   B.y0 = y0;
   B.cols = x1 - x0;
   B.rows = y1 - y0;
-  B.out = (char *)A.out + plane * (int64_t)A.LH * A.LW * EB;
+  B.out = (char *)A.out + plane * (int64_t)uniform(T.LH) * B.LW * EB;
 #pragma unroll
   for (int i = 0; i < kRampMaxCover; ++i)
 #pragma unroll
@@ -223,14 +247,14 @@ __global__ __launch_bounds__(SB_RAMP_THREADS) void ramp_blend_kernel(const RampA
       if (i < nh && j < nw) {
         const int ti = i0 + i, tj = j0 + j;
         // element (y, x) of the output at tile element (y - oh, x - ow)
-        const int64_t base = (plane * A.sh[ti] - A.oh[ti]) * (int64_t)A.sw[tj] - A.ow[tj];
-        B.tile[i][j] = (const char *)A.ptr[(ti - A.ib) * A.n_w + tj] + base * EB;
+        const int64_t base = (plane * T.sh[ti] - T.oh[ti]) * (int64_t)T.sw[tj] - T.ow[tj];
+        B.tile[i][j] = uniform((const char *)A.ptr[uniform((ti - T.ib) * T.n_w + tj)] + base * EB);
       } else {
         B.tile[i][j] = nullptr;
       }
     }
 #pragma unroll
-  for (int j = 0; j < kRampMaxCover; ++j) B.tw[j] = j < nw ? A.sw[j0 + j] : 0;
+  for (int j = 0; j < kRampMaxCover; ++j) B.tw[j] = j < nw ? uniform(T.sw[j0 + j]) : 0;
 
   // normalised weight tables for the axes with several tiles
   float *ww = lds;
@@ -239,10 +263,10 @@ __global__ __launch_bounds__(SB_RAMP_THREADS) void ramp_blend_kernel(const RampA
   B.wh = wh;
   if (nw > 1)
     for (int q = threadIdx.x; q < B.cols; q += SB_RAMP_THREADS)
-      normalised_weights(x0 + q, j0, nw, A.n_w, A.ow, A.sw, A.mw, A.inv_rw, ww + q, B.cols);
+      normalised_weights(x0 + q, j0, nw, T.n_w, T.ow, T.sw, T.mw, T.inv_rw, ww + q, B.cols);
   if (nh > 1)
     for (int q = threadIdx.x; q < B.rows; q += SB_RAMP_THREADS)
-      normalised_weights(y0 + q, i0, nh, A.n_h, A.oh, A.sh, A.mh, A.inv_rh, wh + q, B.rows);
+      normalised_weights(y0 + q, i0, nh, T.n_h, T.oh, T.sh, T.mh, T.inv_rh, wh + q, B.rows);
   if (nw > 1 || nh > 1) __syncthreads();
 
   const int cls = (nh > 2 || nw > 2) ? 0 : (nh - 1) * 2 + (nw - 1);

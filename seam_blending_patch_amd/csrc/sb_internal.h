@@ -94,9 +94,10 @@ __host__ __device__ constexpr uint32_t ramp_pack(uint32_t p0, uint32_t k0, uint3
   return p0 | (k0 << kRampPosBits) | ((cnt - 1) << 26);
 }
 
-struct RampArgs {
-  void *out;
-  const void *ptr[kMaxWindowTiles];      // tiles of rows [ib, ib + rows): ptr[(i - ib) * n_w + j]
+// The tables a block decodes its work from; each block copies them to LDS
+// with one cooperative load (kernel arguments are not cached, so a chain of
+// dependent reads from them costs a memory round trip each).
+struct alignas(16) RampTables {
   int32_t oh[kRampMaxAxisTiles], sh[kRampMaxAxisTiles]; // H origins and extents
   int32_t ow[kRampMaxAxisTiles], sw[kRampMaxAxisTiles]; // W origins and extents
   uint32_t chunk[kRampMaxChunks + 1];    // packed column chunks; the entry after the last holds its end
@@ -106,6 +107,14 @@ struct RampArgs {
   int32_t LH, LW, rows_pb;
   int32_t mh, mw;                        // margins
   float inv_rh, inv_rw;                  // 1 / ramp
+};
+static_assert(sizeof(RampTables) % 16 == 0, "copied in 16-byte pieces");
+static_assert(sizeof(RampTables) <= 16 * 256, "copied by one block in one pass");
+
+struct RampArgs {
+  RampTables t;
+  void *out;
+  const void *ptr[kMaxWindowTiles];      // tiles of rows [ib, ib + rows): ptr[(i - ib) * n_w + j]
 };
 
 } // namespace sb

@@ -55,6 +55,14 @@ def test_config_full_size_bitexact(sb, cfg):
     compare.assert_bitexact(from_dev(out, w.dtype), want, w.dtype, f"config {cfg} poisoned out")
 
 
+@pytest.mark.parametrize("name", sorted(workloads.ENCODE_BLEND_WORKLOADS))
+def test_stock_tiled_encode_latents_bitexact(sb, name):
+    # the same blend on encoder outputs: 4-channel latent tiles of 64 with a
+    # 16-latent blend and a sliver at the edge
+    w = workloads.ENCODE_BLEND_WORKLOADS[name]
+    check(sb, w, workloads.draw_tiles(w), "encode")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("ndim", [4, 5])
 def test_random_grids_vector_path(sb, dtype, ndim):

@@ -360,6 +360,19 @@ RAMP_WORKLOADS = {
 }
 
 
+# Stock tiled encode of an SD-class AutoencoderKL (8x, 4 latent channels): 512 px
+# sample tiles at a 384 px stride give 64-latent tiles every 48 latents, blended
+# over 16 latents; a 2048 px image is 256 latents, the last tile a 16-latent sliver.
+ENCODE_BLEND_WORKLOADS = {
+    "sd-encode-2048-fp16": BlendWorkload(
+        "sd-encode-2048-fp16", "fp16", 4, 1, 4, [1], stock_layout(256, 64, 48),
+        stock_layout(256, 64, 48), (0, 16, 16), (1, 48, 48), seed=25, std=1.0, clamp=None),
+    "sd-encode-4096-bf16-batch4": BlendWorkload(
+        "sd-encode-4096-bf16-batch4", "bf16", 4, 4, 4, [1], stock_layout(512, 64, 48),
+        stock_layout(512, 64, 48), (0, 16, 16), (1, 48, 48), seed=26, std=1.0, clamp=None),
+}
+
+
 def draw_ramp_tiles(w: RampWorkload, rng: Optional[np.random.Generator] = None):
     """Tiles in raster order (i, j); each N(0, std), optionally clamped."""
     rng = rng if rng is not None else np.random.default_rng(w.seed)
