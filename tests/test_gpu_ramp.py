@@ -162,3 +162,31 @@ def test_output_buffer_and_graph_replay(sb):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+# Qwen-Image-2.1 (16x) at the sizes of the pages' real-weight checks, in the
+# 32-latent floor tiles placed by the library's planner, and FLUX.1 (8x) at
+# 1600 px in the fewest-calls tiles: planner and blend together, against the
+# oracle's layout and the oracle's blend
+PAGES_SIZES = [((1024, 1024), 16, "edge_aligned", [32, 16]),
+               ((1344, 1344), 16, "edge_aligned", [32, 16]),
+               ((1536, 2752), 16, "edge_aligned", [32, 16]),
+               ((864, 1184), 16, "edge_aligned", [32, 16]),
+               ((2048, 2048), 16, "edge_aligned", [32, 16]),
+               ((1600, 1600), 8, "fewest_calls", [128, 96, 32, 128])]
+
+
+@pytest.mark.parametrize("size,ratio,rule,params", PAGES_SIZES, ids=lambda v: str(v))
+def test_planner_layouts_blend_at_the_pages_sizes(sb, size, ratio, rule, params):
+    from oracle import layout as ol
+    axes = []
+    for px in size:
+        L = px // ratio
+        o, e = sb.vae_tile_layout(L, rule, params)
+        assert list(zip(o, e)) == ol.layout(L, rule, params)
+        axes.append(([v * ratio for v in o], [v * ratio for v in e]))
+    (oh, eh), (ow, ew) = axes
+    w = W.RampWorkload(f"pages-{size[0]}x{size[1]}", "bf16", (1, 3), oh, eh, ow, ew, (4 * ratio,) * 2,
+                       (8 * ratio,) * 2, seed=size[0] + size[1])
+    assert w.out_shape[-2:] == tuple(size)
+    check(sb, w, "planner+blend")
