@@ -232,16 +232,49 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   const int64_t per_block = std::min<int64_t>(
       SB_BLEND_PER_BLOCK_MAX,
       std::max<int64_t>(SB_BLEND_PER_BLOCK_MIN, total_vec / ((int64_t)cus * SB_BLEND_BLOCKS_PER_CU)));
-  int64_t rows_pb = std::max<int64_t>(1, std::min<int64_t>(1024, per_block / seg_max));
+  // Span layout when every W segment is narrow (fewer than SB_BLEND_SPAN_BELOW
+  // vectors): a block then owns whole tile columns, about 128 vectors of a row.
+#ifndef SB_BLEND_SPAN_BELOW
+#define SB_BLEND_SPAN_BELOW 16
+#endif
+  const bool span = Aw.n >= 2 && seg_max < SB_BLEND_SPAN_BELOW;
+  int64_t span_k = 0, n_spans = 0, span_w = 0;
+  if (span) {
+    const int64_t col_vec = std::max<int64_t>(1, Aw.R / V);
+#ifndef SB_BLEND_SPAN_VECS
+#define SB_BLEND_SPAN_VECS 128
+#endif
+    span_k = std::min<int64_t>({(int64_t)sb::kMaxSpanCols, Aw.n,
+                                std::max<int64_t>(1, (SB_BLEND_SPAN_VECS + col_vec - 1) / col_vec)});
+    n_spans = (Aw.n + span_k - 1) / span_k;
+    for (int64_t s = 0; s < n_spans; ++s) {
+      const int64_t ja = s * span_k, jb = std::min(ja + span_k, Aw.n);
+      span_w = std::max(span_w, (jb == Aw.n ? Aw.L : jb * Aw.R) - ja * Aw.R);
+    }
+  }
+#ifndef SB_BLEND_SPAN_PER_BLOCK_MIN
+#define SB_BLEND_SPAN_PER_BLOCK_MIN 512
+#endif
+  const int64_t block_cols = span ? span_w / V : seg_max;
+  const int64_t per_block_l = span ? std::min<int64_t>(
+                                         SB_BLEND_PER_BLOCK_MAX,
+                                         std::max<int64_t>(SB_BLEND_SPAN_PER_BLOCK_MIN,
+                                                           total_vec / ((int64_t)cus * SB_BLEND_BLOCKS_PER_CU)))
+                                   : per_block;
+  int64_t rows_pb = std::max<int64_t>(1, std::min<int64_t>(1024, per_block_l / block_cols));
   rows_pb = std::min<int64_t>(rows_pb, Ah.L);
   {
     const int64_t nrb = (Ah.L + rows_pb - 1) / rows_pb;
     rows_pb = (Ah.L + nrb - 1) / nrb;
   }
   A.rows_per_block = (int32_t)rows_pb;
-  const size_t lds = (size_t)(ew_max + rows_pb) * sizeof(float2);
+  A.span_k = (int32_t)span_k;
+  A.span_w = (int32_t)span_w;
+  A.div_Rw = sb::make_fastdiv((uint32_t)Aw.R);
+  const size_t lds = span ? (size_t)(span_w + rows_pb) * sizeof(float2) + (size_t)span_k * sizeof(sb::SpanCol)
+                          : (size_t)(ew_max + rows_pb) * sizeof(float2);
   hipStream_t st = (hipStream_t)stream;
-  const int64_t n_wseg = 2 * Aw.n - 1;
+  const int64_t n_wseg = span ? n_spans : 2 * Aw.n - 1;
 
   // Launch windows.  A window covers output frames of temporal tiles
   // [t0, t1) and rows of tile rows [i0, i1); it needs the tile pointers of
@@ -276,13 +309,14 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
       A.Y0 = (int32_t)Y0; A.nY = (int32_t)(Y1 - Y0);
       A.div_nF = sb::make_fastdiv((uint32_t)A.nF);
       const int64_t row_blocks = (A.nY + rows_pb - 1) / rows_pb;
-      // grid x = (plane, frame) pairs of this window, y = W segments, z = row bands
+      // grid x = (plane, frame) pairs of this window, y = W segments (or spans), z = row bands
       const int64_t max_planes = std::max<int64_t>(1, ((int64_t)1 << 30) / A.nF);
       for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
         const int64_t np = std::min(max_planes, planes - p0);
         A.plane0 = (int32_t)p0;
         const dim3 grid((unsigned)(np * A.nF), (unsigned)n_wseg, (unsigned)row_blocks);
-        hipError_t e = sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid, lds, st);
+        hipError_t e = span ? sb_launch_blend_span(A, dtype, vec16 ? 1 : 0, grid, lds, st)
+                            : sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid, lds, st);
         if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
       }
       i0 = i1;

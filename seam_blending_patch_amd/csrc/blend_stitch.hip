@@ -406,6 +406,257 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_ke
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Span layout, for narrow seams.  When every W segment is only a few vectors
+// wide (small blend extents and row limits, as in tiled-encode latents), one
+// segment per block leaves each wavefront reading short row pieces of many
+// rows.  Here a block owns a span of whole tile columns instead and walks its
+// rows left to right, so consecutive lanes read consecutive vectors; the
+// column class (seam or body) and the tile column vary per lane, the row and
+// frame classes stay block-uniform per run.  Same closed form, same
+// arithmetic, element by element through fp32.
+// ---------------------------------------------------------------------------
+struct SpanRun {
+  char *o;                       // output at (local row 0, first column of the span)
+  int64_t opitch;
+  int y0, y1;                    // local rows of the tile row
+  int xs0, wv, ja, nw;           // first output column, vectors per row, first tile column, n_w
+  float inv_wv;
+  FastDiv div_Rw;
+  const float2 *ch, *cw;         // row coefficients by local row; column coefficients by span column
+  float2 ct;
+};
+
+template <int DT, int VB, bool HS, bool TS>
+__device__ __forceinline__ void span_rows(const SpanRun &R, const SpanCol *cols, int tid, int nthreads) {
+  constexpr int V = VecInfo<DT, VB>::V;
+  constexpr int EB = Elem<DT>::bytes;
+  constexpr int U = 2; // output vectors per thread per batch
+  const int nvec = (R.y1 - R.y0) * R.wv;
+  for (int q0 = tid; q0 < nvec; q0 += nthreads * U) {
+    Vec<VB> m[U], up[U], lf[U], cn[U], pm[U], pu[U], pl[U], pc[U];
+    int yy[U], xs[U];
+    bool ok[U], ws[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int q = q0 + k * nthreads;
+      ok[k] = q < nvec;
+      int r = (int)((float)q * R.inv_wv);
+      r -= (r * R.wv > q) ? 1 : 0;
+      r += ((r + 1) * R.wv <= q) ? 1 : 0;
+      const int y = R.y0 + r;
+      const int xo = (q - r * R.wv) * V;             // column within the span
+      const int x = R.xs0 + xo;                      // output column
+      const int j = min((int)fdiv((uint32_t)x, R.div_Rw), R.nw - 1);
+      yy[k] = y;
+      xs[k] = xo;
+      ws[k] = false;
+      if (ok[k]) {
+        const SpanCol &C = cols[j - R.ja];
+        const int xl = x - C.xbase;                  // column within tile j
+        ws[k] = xl < C.ews;
+        const int64_t oj = (int64_t)y * C.pitch_j + (int64_t)xl * EB;
+        const int64_t op = (int64_t)y * C.pitch_p + (int64_t)xl * EB;
+        m[k] = vload<VB, SB_BLEND_NT>(C.m + oj);
+        if constexpr (HS) up[k] = vload<VB, SB_BLEND_NT>(C.u + oj);
+        if (ws[k]) {
+          lf[k] = vload<VB, SB_BLEND_NT>(C.l + op);
+          if constexpr (HS) cn[k] = vload<VB, SB_BLEND_NT>(C.c + op);
+        }
+        if constexpr (TS) {
+          pm[k] = vload<VB, SB_BLEND_NT>(C.pm + oj);
+          if constexpr (HS) pu[k] = vload<VB, SB_BLEND_NT>(C.pu + oj);
+          if (ws[k]) {
+            pl[k] = vload<VB, SB_BLEND_NT>(C.pl + op);
+            if constexpr (HS) pc[k] = vload<VB, SB_BLEND_NT>(C.pc + op);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      if (!ok[k]) continue;
+      char *dst = R.o + (int64_t)yy[k] * R.opitch + (int64_t)xs[k] * EB;
+      if (!HS && !TS && !ws[k]) {
+        vstore<VB, SB_BLEND_NT_STORE>(dst, m[k]);
+        continue;
+      }
+      float2 chh = make_float2(0.f, 0.f);
+      if constexpr (HS) chh = R.ch[yy[k]];
+      float2 cww[V];
+      if (ws[k]) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) cww[e] = R.cw[xs[k] + e];
+      }
+      const bool w = ws[k];
+      auto spatial = [&](const Vec<VB> &vm, const Vec<VB> &vu, const Vec<VB> &vl, const Vec<VB> &vc,
+                         float *o) {
+        unpack<DT, VB>(vm, o);
+        if constexpr (HS) {
+          float Uv[V];
+          unpack<DT, VB>(vu, Uv);
+          if (w) {
+            float Cn[V];
+            unpack<DT, VB>(vc, Cn);
+#pragma unroll
+            for (int e = 0; e < V; ++e) Uv[e] = crossfade<DT>(Cn[e], Uv[e], cww[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < V; ++e) o[e] = crossfade<DT>(Uv[e], o[e], chh);
+        }
+        if (w) {
+          float Lf[V];
+          unpack<DT, VB>(vl, Lf);
+          if constexpr (HS) {
+            float Cn[V];
+            unpack<DT, VB>(vc, Cn);
+#pragma unroll
+            for (int e = 0; e < V; ++e) Lf[e] = crossfade<DT>(Cn[e], Lf[e], chh);
+          }
+#pragma unroll
+          for (int e = 0; e < V; ++e) o[e] = crossfade<DT>(Lf[e], o[e], cww[e]);
+        }
+      };
+      float S[V];
+      spatial(m[k], up[k], lf[k], cn[k], S);
+      if constexpr (TS) {
+        float Sp[V];
+        spatial(pm[k], pu[k], pl[k], pc[k], Sp);
+#pragma unroll
+        for (int e = 0; e < V; ++e) S[e] = crossfade<DT>(Sp[e], S[e], R.ct);
+      }
+      vstore<VB, SB_BLEND_NT_STORE>(dst, pack<DT, VB>(S));
+    }
+  }
+}
+
+template <int DT, int VB>
+__global__ __launch_bounds__(SB_BLEND_THREADS) void blend_span_kernel(const BlendArgs A) {
+  constexpr int EB = Elem<DT>::bytes;
+  // LDS: [span_w] column coefficients, [rows_per_block] row coefficients, [span_k] SpanCol
+  extern __shared__ float2 s_tab[];
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int nw = A.n_w, nh = A.n_h, nt = A.n_t;
+
+  // ---- span: tile columns [ja, jb) ----
+  const int ja = blockIdx.y * A.span_k;
+  const int jb = min(ja + A.span_k, nw);
+  const int xs0 = ja * A.R[2];
+  const int xs1 = jb == nw ? A.LW : jb * A.R[2];
+
+  // ---- frame (block-uniform), as in blend_stitch_kernel ----
+  const uint32_t pz = blockIdx.x;
+  const uint32_t pli = fdiv(pz, A.div_nF);
+  const int64_t plane = (int64_t)A.plane0 + pli;
+  const int f_out = A.F0 + (int)(pz - pli * (uint32_t)A.nF);
+  const int tau = min((int)fdiv((uint32_t)f_out, A.div_Rt), nt - 1);
+  const int f = f_out - tau * A.R[0];
+  const int tt = A.ext[0][tau];
+  const int tp = tau > 0 ? A.ext[0][tau - 1] : 0;
+  const int et = tau > 0 ? min(A.E[0], min(tp, tt)) : 0;
+  const bool ts = f < et;
+  const int fp = tp - et + f;
+
+  const int r0 = blockIdx.z * A.rows_per_block;
+  const int r1 = min(r0 + A.rows_per_block, A.nY);
+  const int yo0 = A.Y0 + r0, yo1 = A.Y0 + r1;
+
+  float2 *s_cw = s_tab;
+  float2 *s_ch = s_tab + A.span_w;
+  SpanCol *s_col = reinterpret_cast<SpanCol *>(s_tab + A.span_w + A.rows_per_block);
+
+  // column coefficients of the span's seams
+  for (int x = xs0 + tid; x < xs1; x += nthr) {
+    const int j = min((int)fdiv((uint32_t)x, A.div_Rw), nw - 1);
+    const int xl = x - j * A.R[2];
+    const int ew = j > 0 ? min(A.E[2], min(A.ext[2][j - 1], A.ext[2][j])) : 0;
+    if (xl < ew) s_cw[x - xs0] = coefficients(xl, ew);
+  }
+  // row coefficients of the band's rows that lie in a row seam
+  if (A.E[1] > 0)
+    for (int k = tid; k < r1 - r0; k += nthr) {
+      const int yo = yo0 + k;
+      const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
+      const int y = yo - i * A.R[1];
+      const int eh = i > 0 ? min(A.E[1], min(A.ext[1][i - 1], A.ext[1][i])) : 0;
+      if (y < eh) s_ch[k] = coefficients(y, eh);
+    }
+  const float2 ct = ts ? coefficients(f, et) : make_float2(0.f, 0.f);
+
+  const char *const *P = (const char *const *)A.ptr;
+  auto tile = [&](int tq, int ti, int tj) {
+    return P[((tq - A.taub) * A.ptr_nh + (ti - A.ib)) * nw + tj];
+  };
+
+  int yo = yo0;
+  while (yo < yo1) {
+    const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
+    const int ybase = i * A.R[1];
+    const int hi = A.ext[1][i];
+    const int hp = i > 0 ? A.ext[1][i - 1] : 0;
+    const int eh = i > 0 ? min(A.E[1], min(hp, hi)) : 0;
+    const int chh = i < nh - 1 ? A.R[1] : hi;
+    const int ehs = min(eh, chh);
+    const int yl = yo - ybase;
+    const bool hs = yl < ehs;
+    const int yl1 = min(hs ? ehs : chh, yl + (yo1 - yo));
+    const int u = hp - eh;
+
+    __syncthreads(); // the previous run is done with s_col (and the tables are written)
+    for (int t = tid; t < jb - ja; t += nthr) {
+      const int j = ja + t;
+      const int wj = A.ext[2][j];
+      const int wp = j > 0 ? A.ext[2][j - 1] : 0;
+      const int ew = j > 0 ? min(A.E[2], min(wp, wj)) : 0;
+      const int cw = j < nw - 1 ? A.R[2] : wj;
+      const int l = wp - ew;
+      const int64_t pj = (int64_t)wj * EB, pp = (int64_t)wp * EB;
+      SpanCol C;
+      C.pitch_j = pj;
+      C.pitch_p = pp;
+      C.xbase = j * A.R[2];
+      C.ews = min(ew, cw);
+      C.m = tile(tau, i, j) + ((plane * tt + f) * hi) * pj;
+      C.u = C.l = C.c = C.pm = C.pu = C.pl = C.pc = nullptr;
+      if (hs) C.u = tile(tau, i - 1, j) + ((plane * tt + f) * hp + u) * pj;
+      if (ew > 0) C.l = tile(tau, i, j - 1) + ((plane * tt + f) * hi) * pp + (int64_t)l * EB;
+      if (hs && ew > 0) C.c = tile(tau, i - 1, j - 1) + ((plane * tt + f) * hp + u) * pp + (int64_t)l * EB;
+      if (ts) {
+        C.pm = tile(tau - 1, i, j) + ((plane * tp + fp) * hi) * pj;
+        if (hs) C.pu = tile(tau - 1, i - 1, j) + ((plane * tp + fp) * hp + u) * pj;
+        if (ew > 0) C.pl = tile(tau - 1, i, j - 1) + ((plane * tp + fp) * hi) * pp + (int64_t)l * EB;
+        if (hs && ew > 0)
+          C.pc = tile(tau - 1, i - 1, j - 1) + ((plane * tp + fp) * hp + u) * pp + (int64_t)l * EB;
+      }
+      s_col[t] = C;
+    }
+    __syncthreads();
+
+    SpanRun R;
+    R.o = (char *)A.out + (((plane * A.LT + f_out) * A.LH + ybase) * (int64_t)A.LW + xs0) * EB;
+    R.opitch = (int64_t)A.LW * EB;
+    R.y0 = yl;
+    R.y1 = yl1;
+    R.xs0 = xs0;
+    R.wv = (xs1 - xs0) / VecInfo<DT, VB>::V;
+    R.inv_wv = 1.0f / (float)R.wv;
+    R.ja = ja;
+    R.nw = nw;
+    R.div_Rw = A.div_Rw;
+    R.ch = s_ch + (ybase - yo0);
+    R.cw = s_cw;
+    R.ct = ct;
+    const int cls = (ts ? 2 : 0) | (hs ? 1 : 0);
+    switch (cls) {
+      case 0: span_rows<DT, VB, false, false>(R, s_col, tid, nthr); break;
+      case 1: span_rows<DT, VB, true, false>(R, s_col, tid, nthr); break;
+      case 2: span_rows<DT, VB, false, true>(R, s_col, tid, nthr); break;
+      default: span_rows<DT, VB, true, true>(R, s_col, tid, nthr); break;
+    }
+    yo += yl1 - yl;
+  }
+}
 } // namespace sb
 
 hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
@@ -421,6 +672,23 @@ hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 gr
   } else {
     if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_BF16, 16>), grid, b, lds, st, a);
     else hipLaunchKernelGGL((blend_stitch_kernel<DT_BF16, 2>), grid, b, lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t sb_launch_blend_span(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
+                                hipStream_t st) {
+  using namespace sb;
+  dim3 b(SB_BLEND_THREADS);
+  if (dtype == DT_F32) {
+    if (vec16) hipLaunchKernelGGL((blend_span_kernel<DT_F32, 16>), grid, b, lds, st, a);
+    else hipLaunchKernelGGL((blend_span_kernel<DT_F32, 4>), grid, b, lds, st, a);
+  } else if (dtype == DT_F16) {
+    if (vec16) hipLaunchKernelGGL((blend_span_kernel<DT_F16, 16>), grid, b, lds, st, a);
+    else hipLaunchKernelGGL((blend_span_kernel<DT_F16, 2>), grid, b, lds, st, a);
+  } else {
+    if (vec16) hipLaunchKernelGGL((blend_span_kernel<DT_BF16, 16>), grid, b, lds, st, a);
+    else hipLaunchKernelGGL((blend_span_kernel<DT_BF16, 2>), grid, b, lds, st, a);
   }
   return hipGetLastError();
 }

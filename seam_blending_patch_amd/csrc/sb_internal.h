@@ -48,7 +48,21 @@ struct BlendArgs {
   int32_t plane0;                   // first (n, c) plane of this launch
   int32_t rows_per_block;           // output rows per block
   int32_t ew_max;                   // largest column blend extent (LDS table length)
-  FastDiv div_nF, div_Rt, div_Rh;
+  int32_t span_k;                   // span layout: tile columns per span (0: segment layout)
+  int32_t span_w;                   // span layout: widest span in elements (LDS table length)
+  FastDiv div_nF, div_Rt, div_Rh, div_Rw;
+};
+
+constexpr int kMaxSpanCols = 32; // tile columns per span (span layout)
+
+// One tile column of a span (span layout), for one run of rows: the tiles the
+// closed form reads, each offset so that operand (y, x) of the column is at
+// base + y * pitch + x * elem_bytes; built per run in LDS.
+struct SpanCol {
+  const char *m, *u, *l, *c;     // tiles (i,j), (i-1,j), (i,j-1), (i-1,j-1) of chunk tau
+  const char *pm, *pu, *pl, *pc; // the same in chunk tau-1
+  int64_t pitch_j, pitch_p;      // bytes per row of tile column j and j-1
+  int32_t xbase, ews;            // first output column of the column's crop; its seam width
 };
 
 // ---------------------------------------------------------------------------
@@ -122,6 +136,8 @@ struct RampArgs {
 // launchers (defined in the .hip files)
 hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                            hipStream_t st);
+hipError_t sb_launch_blend_span(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
+                                hipStream_t st);
 hipError_t sb_launch_groupnorm(const sb::GNArgs &a, int dtype, int vec16, hipStream_t st);
 hipError_t sb_launch_ramp(const sb::RampArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                           hipStream_t st);
