@@ -22,8 +22,7 @@ __all__ = ["vae_tile_layout", "LAYOUT_RULES", "vae_tile_ramp_blend", "RampBlend"
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseamblend.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
-                      "g.build()' or python seam_blending_patch_amd/build.py)")
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python seam_blending_patch_amd/build.py)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i64p = ctypes.POINTER(ctypes.c_int64)

@@ -15,7 +15,7 @@ blend tiles in raster order (temporal tile, tile row, tile column), then the
 GroupNorm per-patch offsets, x, gamma, beta.
 
 Workload shapes follow the five configurations of the tiled-VAE assembly
-benchmark (stated in the design doc with the readings taken where the pages are
+benchmark (with the readings taken where the pages are
 silent): a 112x112 fp32 toy, an SD-v1-size 1024x1024 fp16 decode, a 2048x2048
 bf16 decode plus a decoder-intermediate GroupNorm, a 49-frame 480x832 bf16
 video decode plus a 5-D GroupNorm, and a 4096x4096 fp16 batch-2 decode with
@@ -363,10 +363,16 @@ RAMP_WORKLOADS = {
 # Stock tiled encode of an SD-class AutoencoderKL (8x, 4 latent channels): 512 px
 # sample tiles at a 384 px stride give 64-latent tiles every 48 latents, blended
 # over 16 latents; a 2048 px image is 256 latents, the last tile a 16-latent sliver.
+# Also the 64-latent tiles with 32-latent overlaps of the wide-tile encode.
 ENCODE_BLEND_WORKLOADS = {
     "sd-encode-2048-fp16": BlendWorkload(
         "sd-encode-2048-fp16", "fp16", 4, 1, 4, [1], stock_layout(256, 64, 48),
         stock_layout(256, 64, 48), (0, 16, 16), (1, 48, 48), seed=25, std=1.0, clamp=None),
+    # the same blend on 16-channel latents in 64-latent tiles with 32-latent
+    # overlaps (the wide-tile encode geometry), stock placement: 128 latents
+    "encode-64-32-2048-bf16": BlendWorkload(
+        "encode-64-32-2048-bf16", "bf16", 4, 1, 16, [1], stock_layout(128, 64, 32),
+        stock_layout(128, 64, 32), (0, 32, 32), (1, 32, 32), seed=27, std=1.0, clamp=None),
     "sd-encode-4096-bf16-batch4": BlendWorkload(
         "sd-encode-4096-bf16-batch4", "bf16", 4, 4, 4, [1], stock_layout(512, 64, 48),
         stock_layout(512, 64, 48), (0, 16, 16), (1, 48, 48), seed=26, std=1.0, clamp=None),
