@@ -55,6 +55,8 @@ int build_grid(const int64_t grid[6], const int64_t *tile_extents, const int64_t
   G.N = grid[1];
   G.C = grid[2];
   if (G.N < 0 || G.C < 0) return fail(SB_EARG, "N and C must be >= 0");
+  if (G.N >= ((int64_t)1 << 31) || G.C >= ((int64_t)1 << 31) || G.N * G.C >= ((int64_t)1 << 31))
+    return fail(SB_EGEOM, "N * C must be below 2^31");
   const char *names[3] = {"t", "h", "w"};
   int64_t off = 0;
   for (int a = 0; a < 3; ++a) {
@@ -150,6 +152,8 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
     return fail(SB_EARG, "unknown dtype %d", dtype);
   const Axis &At = G.ax[0], &Ah = G.ax[1], &Aw = G.ax[2];
   const int64_t planes = G.N * G.C;
+  if (planes > 0 && At.L * Ah.L * Aw.L > (((int64_t)1 << 50) / planes))
+    return fail(SB_EGEOM, "output too large (more than 2^50 elements)");
   const int EB = elem_bytes(dtype);
   const int64_t ntiles = At.n * Ah.n * Aw.n;
   if (planes == 0) return SB_OK; // nothing to read or write (empty tensors may have null data)

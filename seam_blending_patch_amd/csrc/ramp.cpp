@@ -183,8 +183,11 @@ extern "C" int vae_tile_ramp_blend(const void *const *tiles, const int64_t grid[
   if ((rc = element_runs("h", H, hr))) return rc;
   if ((rc = element_runs("w", W, wr_el))) return rc;
 
+  if (N >= ((int64_t)1 << 31) || C >= ((int64_t)1 << 31) || T >= ((int64_t)1 << 31))
+    return sb_fail_message(SB_EGEOM, "N, C and frames must be below 2^31");
   const int64_t planes = N * C * T;
   if (planes >= ((int64_t)1 << 31)) return sb_fail_message(SB_EGEOM, "N * C * frames must be below 2^31");
+  // (planes < 2^31 and both canvas extents < 2^20: every byte offset below fits in 64 bits)
   if (planes == 0) return SB_OK; // nothing to read or write
   const int EB = dtype == SB_F32 ? 4 : 2;
   const int64_t ntiles = n_h * n_w;

@@ -170,3 +170,23 @@ def test_ramp_rejects_bad_pointers_on_host(sb):
     assert b"overlaps" in lib.seamblend_last_error()
     # an empty batch is a no-op before any pointer is looked at
     assert _ramp_call(lib, (4, 0, 3, 1, 1, 2), o, e, out=0, ptrs=(ctypes.c_void_p * 2)(0, 0)) == 0
+
+
+def test_sizes_beyond_the_index_range_are_rejected_on_host(sb):
+    # N * C at 2^31 or more, or an output beyond 2^50 elements: rejected
+    # before any pointer is used
+    with pytest.raises(sb.SeamBlendError) as ei:
+        sb.vae_tile_blend_stitch_output_extents((4, 1 << 31, 1, 1, 2, 2), [1, 64, 64, 64, 64], (0, 16, 16),
+                                                (1, 48, 48))
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    lib.vae_tile_blend_stitch.restype = ctypes.c_int
+    i64 = lambda v: (ctypes.c_int64 * len(v))(*v)  # noqa: E731
+    fake = (ctypes.c_void_p * 4)(0x1000, 0x100000, 0x200000, 0x300000)
+    assert lib.vae_tile_blend_stitch(fake, i64([4, 1 << 31, 3, 1, 2, 2]), i64([1, 64, 64, 64, 64]),
+                                     i64([0, 16, 16]), i64([1, 48, 48]), 1, ctypes.c_void_p(0x900000),
+                                     None) == -2
+    assert lib.vae_tile_blend_stitch(fake, i64([4, 1 << 20, 1 << 10, 1, 2, 2]),
+                                     i64([1, 1 << 20, 1 << 20, 64, 64]), i64([0, 16, 16]),
+                                     i64([1, 1 << 20, 48]), 1, ctypes.c_void_p(0x900000), None) == -2
+    lib.vae_tile_ramp_blend.restype = ctypes.c_int
+    assert _ramp_call(lib, (5, 1 << 16, 1 << 16, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32]) == -2
