@@ -109,8 +109,7 @@ __host__ __device__ constexpr uint32_t ramp_pack(uint32_t p0, uint32_t k0, uint3
 }
 
 // The tables a block decodes its work from; each block copies them to LDS
-// with one cooperative load (kernel arguments are not cached, so a chain of
-// dependent reads from them costs a memory round trip each).
+// with one cooperative load and does its lookups there.
 struct alignas(16) RampTables {
   int32_t oh[kRampMaxAxisTiles], sh[kRampMaxAxisTiles]; // H origins and extents
   int32_t ow[kRampMaxAxisTiles], sw[kRampMaxAxisTiles]; // W origins and extents
