@@ -190,3 +190,31 @@ def test_planner_layouts_blend_at_the_pages_sizes(sb, size, ratio, rule, params)
                        (8 * ratio,) * 2, seed=size[0] + size[1])
     assert w.out_shape[-2:] == tuple(size)
     check(sb, w, "planner+blend")
+
+
+def test_deterministic_and_concurrent(sb):
+    # two runs give identical bits; two layouts on two streams at once give the
+    # serial results
+    plans, serial = [], []
+    for name in ("qwen21-2048-bf16", "flux-1600-bf16"):
+        w = W.RAMP_WORKLOADS[name]
+        grid = dev_grid(w, W.draw_ramp_tiles(w))
+        p = sb.RampBlend(grid, w.origins_h, w.origins_w, w.margin, w.ramp)
+        a = p().clone()
+        b = p().clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        plans.append((p, grid))
+        serial.append(a)
+    for p, _ in plans:
+        p.out.zero_()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for (p, _), st in zip(plans, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            for _ in range(3):
+                p()
+    torch.cuda.synchronize()
+    for (p, _), want in zip(plans, serial):
+        assert torch.equal(p.out.view(torch.int16), want.view(torch.int16))
