@@ -75,6 +75,8 @@ int build_grid(const int64_t grid[6], const int64_t *tile_extents, const int64_t
     }
     if (A.E < 0) return fail(SB_EARG, "blend extent along %s must be >= 0", names[a]);
     if (A.R < 1) return fail(SB_EARG, "row limit along %s must be >= 1", names[a]);
+    if (A.R > ((int64_t)1 << 30)) return fail(SB_EARG, "row limit along %s must be <= 2^30", names[a]);
+    A.E = std::min<int64_t>(A.E, (int64_t)1 << 30); // extents are <= 2^30: the clamp e = min(E, ...) is unchanged
     A.ext.assign(tile_extents + off, tile_extents + off + A.n);
     off += A.n;
     for (int64_t k = 0; k < A.n; ++k) {
@@ -152,8 +154,16 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
     return fail(SB_EARG, "unknown dtype %d", dtype);
   const Axis &At = G.ax[0], &Ah = G.ax[1], &Aw = G.ax[2];
   const int64_t planes = G.N * G.C;
-  if (planes > 0 && At.L * Ah.L * Aw.L > (((int64_t)1 << 50) / planes))
-    return fail(SB_EGEOM, "output too large (more than 2^50 elements)");
+  if (planes > 0) {
+    // output and every tile below 2^50 elements: all byte offsets fit in 64 bits
+    int64_t mt = 0, mh = 0, mw = 0;
+    for (int64_t k = 0; k < At.n; ++k) mt = std::max(mt, At.ext[k]);
+    for (int64_t k = 0; k < Ah.n; ++k) mh = std::max(mh, Ah.ext[k]);
+    for (int64_t k = 0; k < Aw.n; ++k) mw = std::max(mw, Aw.ext[k]);
+    const int64_t lim = ((int64_t)1 << 50) / planes;
+    if (At.L * Ah.L > lim / Aw.L || mt * mh > lim / mw)
+      return fail(SB_EGEOM, "output or tile too large (more than 2^50 elements)");
+  }
   const int EB = elem_bytes(dtype);
   const int64_t ntiles = At.n * Ah.n * Aw.n;
   if (planes == 0) return SB_OK; // nothing to read or write (empty tensors may have null data)

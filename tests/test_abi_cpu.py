@@ -190,3 +190,15 @@ def test_sizes_beyond_the_index_range_are_rejected_on_host(sb):
                                      i64([1, 1 << 20, 48]), 1, ctypes.c_void_p(0x900000), None) == -2
     lib.vae_tile_ramp_blend.restype = ctypes.c_int
     assert _ramp_call(lib, (5, 1 << 16, 1 << 16, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32]) == -2
+
+
+def test_row_limit_and_blend_extent_beyond_32_bits(sb):
+    # a row limit above 2^30 is rejected (it would not fit the kernel's 32-bit
+    # index arithmetic); a huge blend extent is the same as one clamped to the
+    # tile extents
+    with pytest.raises(sb.SeamBlendError) as ei:
+        sb.vae_tile_blend_stitch_output_extents((4, 1, 3, 1, 1, 1), [1, 64, 64], (0, 16, 16),
+                                                (1, 1 << 32, 48))
+    assert ei.value.code == -1
+    assert sb.vae_tile_blend_stitch_output_extents((4, 1, 3, 1, 2, 2), [1, 64, 64, 64, 64],
+                                                   (0, 1 << 40, 1 << 40), (1, 48, 48)) == (1, 112, 112)
