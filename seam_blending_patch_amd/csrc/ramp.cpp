@@ -187,7 +187,8 @@ extern "C" int vae_tile_ramp_blend(const void *const *tiles, const int64_t grid[
     return sb_fail_message(SB_EGEOM, "N, C and frames must be below 2^31");
   const int64_t planes = N * C * T;
   if (planes >= ((int64_t)1 << 31)) return sb_fail_message(SB_EGEOM, "N * C * frames must be below 2^31");
-  // (planes < 2^31 and both canvas extents < 2^20: every byte offset below fits in 64 bits)
+  if (planes > 0 && H.L * W.L > ((int64_t)1 << 50) / planes)
+    return sb_fail_message(SB_EGEOM, "output too large (more than 2^50 elements)");
   if (planes == 0) return SB_OK; // nothing to read or write
   const int EB = dtype == SB_F32 ? 4 : 2;
   const int64_t ntiles = n_h * n_w;

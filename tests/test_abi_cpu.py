@@ -202,3 +202,10 @@ def test_row_limit_and_blend_extent_beyond_32_bits(sb):
     assert ei.value.code == -1
     assert sb.vae_tile_blend_stitch_output_extents((4, 1, 3, 1, 2, 2), [1, 64, 64, 64, 64],
                                                    (0, 1 << 40, 1 << 40), (1, 48, 48)) == (1, 112, 112)
+
+
+def test_ramp_output_beyond_2_50_elements_is_rejected(sb):
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    lib.vae_tile_ramp_blend.restype = ctypes.c_int
+    big = (1 << 19) + 16
+    assert _ramp_call(lib, (4, 1 << 15, 1 << 15, 1, 1, 2), [0, 0, 0, 16], [1, big, 32, 32]) == -2
