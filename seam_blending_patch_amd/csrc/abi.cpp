@@ -365,10 +365,16 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
     return fail(SB_EARG, "split_axis must be a spatial axis (2..%d), got %d", ndim - 1, split_axis);
   if (n_patches < 1 || n_patches > sb::kMaxPatches)
     return fail(SB_EARG, "n_patches must be in 1..%d", sb::kMaxPatches);
+  if (shape[0] > ((int64_t)1 << 20) || shape[1] > ((int64_t)1 << 24))
+    return fail(SB_EGEOM, "N or C too large");
   sb::GNArgs &a = P.a;
   std::memset(&a, 0, sizeof a);
   int64_t S = 1;
-  for (int k = 2; k < ndim; ++k) S *= shape[k];
+  for (int k = 2; k < ndim; ++k) {
+    if (shape[k] > ((int64_t)1 << 30) || (shape[k] > 0 && S > ((int64_t)1 << 40) / shape[k]))
+      return fail(SB_EGEOM, "spatial extents too large (each <= 2^30, product <= 2^40)");
+    S *= shape[k];
+  }
   a.N = (int32_t)shape[0];
   a.C = (int32_t)shape[1];
   a.G = (int32_t)groups;
@@ -385,8 +391,6 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
   a.n_big = (int32_t)(a.L % n_patches);
   a.len_big = a.len_small + 1;
   P.empty = shape[0] == 0 || shape[1] == 0 || S == 0;
-  if (shape[0] > ((int64_t)1 << 20) || shape[1] > ((int64_t)1 << 24))
-    return fail(SB_EGEOM, "N or C too large");
   // vector width: every run of a patch and every plane a whole number of
   // 16-byte vectors (base alignment is checked per call)
   const int V16 = 16 / dtype_bytes;

@@ -17,6 +17,7 @@
 //    max(floor, T) with overlap max(floor overlap, T - S).
 // "Spread evenly" is read as origin_k = floor(k (L - t) / (n - 1)).
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -25,6 +26,11 @@
 extern "C" int sb_fail_message(int code, const char *msg); // abi.cpp
 
 namespace {
+
+// lengths, tiles, strides and overlaps are at most 2^30 positions: every sum
+// and product below stays far inside 64 bits, and a stride of 1 over the
+// longest canvas is 2^30 tiles, which max_tiles bounds before any loop runs
+constexpr int64_t kMaxLength = (int64_t)1 << 30;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -59,8 +65,11 @@ int stock(int64_t L, int64_t T, int64_t S, int64_t max_tiles, int64_t *o, int64_
 extern "C" int vae_tile_layout(int64_t L, int rule, const int64_t params[4], int64_t max_tiles,
                                int64_t *origins, int64_t *extents, int64_t *n_tiles) {
   if (!params || !origins || !extents || !n_tiles) return sb_fail_message(SB_EARG, "null pointer");
-  if (L < 1) return sb_fail_message(SB_EARG, "canvas length must be >= 1");
+  if (L < 1 || L > kMaxLength) return sb_fail_message(SB_EARG, "canvas length must be in 1..2^30");
   if (max_tiles < 1) return sb_fail_message(SB_EARG, "max_tiles must be >= 1");
+  for (int k = 0; k < 4; ++k)
+    if (params[k] < 0 || params[k] > kMaxLength)
+      return sb_fail_message(SB_EARG, "layout parameters must be in 0..2^30");
   int rc = -1;
   switch (rule) {
     case SB_LAYOUT_STOCK: {
@@ -84,8 +93,12 @@ extern "C" int vae_tile_layout(int64_t L, int rule, const int64_t params[4], int
     case SB_LAYOUT_FEWEST_CALLS: {
       const int64_t T = params[0], S = params[1], ov = params[2], M = params[3];
       if (T < 1 || S < 1 || S > T || ov < 0 || M < 1) return sb_fail_message(SB_EARG, "bad fewest-calls parameters");
-      int64_t budget = 0; // latents the stock loop decodes along the axis
-      for (int64_t k = 0; k * S < L; ++k) budget += (T < L - k * S) ? T : L - k * S;
+      // latents the stock loop decodes along the axis: n_s tiles, the full
+      // ones of T and the rest cut short by the edge
+      const int64_t n_s = ceil_div(L, S);
+      const int64_t n_full = std::min(n_s, L >= T ? (L - T) / S + 1 : 0);
+      const int64_t m = n_s - n_full; // the cut tiles k = n_full .. n_s - 1 have extents L - kS
+      const int64_t budget = n_full * T + m * L - S * ((n_full + n_s - 1) * m / 2);
       if (L <= M) { // one call over the whole canvas (the stock loop decodes >= L)
         origins[0] = 0;
         extents[0] = L;
@@ -96,21 +109,24 @@ extern "C" int vae_tile_layout(int64_t L, int rule, const int64_t params[4], int
       // the widest side within the budget is min(M, budget / n); when even the
       // smallest covering side exceeds it, that side is still taken if the
       // exact fractional covering (L + (n - 1) ov latents) fits the budget
-      for (int64_t n = 2; n <= L && n <= max_tiles; ++n) {
-        const int64_t t_cov = ceil_div(L + (n - 1) * ov, n);
-        if (t_cov > M || t_cov <= ov) continue;
-        int64_t t = budget / n;
-        if (t > M) t = M;
-        if (t > L) t = L;
-        if (t < t_cov) {
-          if (L + (n - 1) * ov > budget) continue;
-          t = t_cov;
+      // The fewest tiles of side <= M that cover: t_cov <= M iff n >= (L - ov) / (M - ov).
+      // From there, n tiles decode at least L + (n - 1) ov latents, which only
+      // grows with n: once that exceeds the budget, no larger n fits either.
+      if (M > ov && L > ov) {
+        for (int64_t n = std::max<int64_t>(2, ceil_div(L - ov, M - ov)); n <= L; ++n) {
+          if (L + (n - 1) * ov > budget) break;
+          const int64_t t_cov = ceil_div(L + (n - 1) * ov, n);
+          if (t_cov > M || t_cov <= ov) continue;
+          int64_t t = budget / n;
+          if (t > M) t = M;
+          if (t > L) t = L;
+          if (t < t_cov) t = t_cov; // up to rounding: the exact covering fits the budget
+          rc = spread(L, t, n, max_tiles, origins, extents);
+          if (rc < 0) return rc; // more tiles than max_tiles
+          break;
         }
-        rc = spread(L, t, n, max_tiles, origins, extents);
-        break;
       }
-      if (rc < 0)
-        return sb_fail_message(SB_EGEOM, "no layout of at most max_tiles tiles decodes within the stock budget");
+      if (rc < 0) return sb_fail_message(SB_EGEOM, "no layout decodes within the stock budget");
       break;
     }
     case SB_LAYOUT_SMALLEST_SIDE: {
@@ -130,17 +146,11 @@ extern "C" int vae_tile_layout(int64_t L, int rule, const int64_t params[4], int
     case SB_LAYOUT_AUTO: {
       const int64_t T = params[0], S = params[1], ft = params[2], fov = params[3];
       if (T < 1 || S < 1 || S > T || ft < 1 || fov < 0) return sb_fail_message(SB_EARG, "bad auto parameters");
-      bool keep = true;
+      // Stock tile k has extent min(T, L - kS) and overlaps the next by
+      // min(T, L - kS) - S: both shrink with k, so the last tile and the last
+      // overlap are the smallest.  A single stock tile covers the canvas.
       const int64_t n = ceil_div(L, S);
-      for (int64_t k = 0; k < n && keep; ++k) {
-        const int64_t ext = (T < L - k * S) ? T : L - k * S;
-        if (ext < ft) keep = false;
-        if (k > 0) {
-          const int64_t prev_end = (k - 1) * S + ((T < L - (k - 1) * S) ? T : L - (k - 1) * S);
-          if (prev_end - k * S < fov) keep = false;
-        }
-      }
-      if (n == 1) keep = true; // a single stock tile covers the canvas
+      const bool keep = n == 1 || (L - (n - 1) * S >= ft && std::min(T, L - (n - 2) * S) - S >= fov);
       if (keep) {
         rc = stock(L, T, S, max_tiles, origins, extents);
       } else {

@@ -64,7 +64,10 @@ int read_axis(const char *name, int64_t n, const int64_t *o, const int64_t *s, i
   A.s.assign(s, s + n);
   if (A.o[0] != 0) return failf(SB_EGEOM, "the first tile along %s must start at 0", name);
   for (int64_t k = 0; k < n; ++k) {
-    if (A.s[k] < 1) return failf(SB_EARG, "tile extent %s[%lld] must be >= 1", name, (long long)k);
+    if (A.s[k] < 1 || A.s[k] >= ((int64_t)1 << sb::kRampPosBits))
+      return failf(SB_EARG, "tile extent %s[%lld] must be in 1..2^20", name, (long long)k);
+    if (A.o[k] < 0 || A.o[k] >= ((int64_t)1 << sb::kRampPosBits))
+      return failf(SB_EGEOM, "tile origin %s[%lld] must be in 0..2^20", name, (long long)k);
     if (k > 0 && A.o[k] <= A.o[k - 1])
       return failf(SB_EGEOM, "tile origins along %s must increase", name);
   }

@@ -168,3 +168,21 @@ def test_library_rejects_a_layout_beyond_capacity(sb):
     with pytest.raises(sb.SeamBlendError) as ei:
         sb.vae_tile_layout(1000, "stock", [2, 1], max_tiles=16)
     assert ei.value.code == -1
+
+
+def test_extreme_parameters_fail_fast(sb):
+    # canvas and parameters beyond 2^30, and layouts with far more tiles than
+    # the output arrays hold, are rejected without walking the tiles
+    import time
+    t0 = time.perf_counter()
+    for rule, L, p in [("fewest_calls", 1 << 30, [1 << 30, 1, 0, 5]),
+                       ("auto", 1 << 30, [1 << 20, 1, 1, 0]),
+                       ("stock", 1 << 30, [2, 1]),
+                       ("edge_aligned", 1 << 30, [2, 1]),
+                       ("smallest_side", 1 << 30, [1, 2]),
+                       ("stock", (1 << 30) + 1, [16, 12]),
+                       ("fewest_calls", 100, [128, 96, 1 << 31, 128]),
+                       ("auto", 100, [16, 12, -1, 0])]:
+        with pytest.raises(sb.SeamBlendError):
+            sb.vae_tile_layout(L, rule, p, max_tiles=64)
+    assert time.perf_counter() - t0 < 1.0
