@@ -221,13 +221,22 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   A.div_Rt = sb::make_fastdiv((uint32_t)At.R);
   A.div_Rh = sb::make_fastdiv((uint32_t)Ah.R);
   A.ew_max = (int32_t)ew_max;
+  {
+    // 32-bit lane offsets when every (plane, frame) slice of a tile and every
+    // band of output rows as tall as a tile stays below 2^31 bytes
+    int64_t mh = 0, mw = 0;
+    for (int64_t k = 0; k < Ah.n; ++k) mh = std::max(mh, Ah.ext[k]);
+    for (int64_t k = 0; k < Aw.n; ++k) mw = std::max(mw, Aw.ext[k]);
+    const int64_t cap = (((int64_t)1 << 31) - 1) / EB;
+    A.off32 = (mh <= cap / std::max<int64_t>(mw, 1) && mh <= cap / std::max<int64_t>(Aw.L, 1)) ? 1 : 0;
+  }
   // Rows per block.  Each block pays a fixed start-up (argument loads, seam
   // coefficient tables, a barrier), so blocks are made as large as the
   // problem allows while still giving every CU several blocks: about
   // total / (cus * SB_BLEND_BLOCKS_PER_CU) vectors in the widest W segment,
   // clamped to [1024, 8192], then balanced over the rows.
 #ifndef SB_BLEND_BLOCKS_PER_CU
-#define SB_BLEND_BLOCKS_PER_CU 8
+#define SB_BLEND_BLOCKS_PER_CU 12
 #endif
   int64_t seg_max = 1;
   for (int64_t k = 0; k < Aw.n; ++k) {

@@ -40,8 +40,8 @@
 // output vectors per thread sized so that about eight 16-byte loads per lane
 // are in flight (interior copy: 8 vectors; row or column seam: 4; corner: 2;
 // with a frame seam, half of that).  Every tile element the output needs is
-// read once (the corner operand once, used twice), every output element is
-// written once, both with nontemporal hints.  The coefficient tables of the
+// read once, with a nontemporal hint (the corner operand once, used twice),
+// and every output element is written once.  The coefficient tables of the
 // block's seams are built in LDS from float64 division.  Every product and
 // sum is a separate fp32 operation (see crossfade below).
 
@@ -132,57 +132,95 @@ struct Run {
   float2 ct;                     // frame coefficient (frame seams)
 };
 
-template <int DT, int VB, bool HS, bool WS, bool TS>
+// Walks the run's (rows x wv) vectors, nthreads apart, U per lane per batch.
+// Each lane keeps its position (row r, vector x) and the byte offsets of that
+// position in tile column j, tile column j-1 and the output, and advances all
+// of them by nthreads vectors with adds and one carry test, so a vector costs
+// a handful of integer operations.  OFF is the offset type: uint32_t when the
+// host has checked that every offset stays below 2^31 bytes (the loads then
+// take a block-uniform base plus a 32-bit lane offset), int64_t otherwise.
+template <int DT, int VB, bool HS, bool WS, bool TS, class OFF>
 __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
   constexpr int L = (1 + (HS ? 1 : 0) + (WS ? 1 : 0) + (HS && WS ? 1 : 0)) * (TS ? 2 : 1);
   constexpr int U = L >= SB_BLEND_LOADS ? 1 : SB_BLEND_LOADS / L; // output vectors per thread per batch
-  const int nvec = (R.y1 - R.y0) * R.wv;
+  const int nrows = R.y1 - R.y0;
+  const int wv = R.wv;
+  // first position: tid / wv exactly (the float quotient is within one of it for tid < 2^24)
+  int r = (int)((float)tid * R.inv_wv);
+  r -= (r * wv > tid) ? 1 : 0;
+  r += ((r + 1) * wv <= tid) ? 1 : 0;
+  int x = tid - r * wv;
+  // one step of nthreads vectors: dr rows and dx vectors, plus a carry row when x passes wv
+  const int dr = nthreads / wv;
+  const int dx = nthreads - dr * wv;
+  const OFF pj = (OFF)R.pitch_j, pp = (OFF)R.pitch_p, po = (OFF)R.opitch;
+  constexpr int VBY = V * EB; // bytes per vector
+  const OFF xstep = (OFF)dx * VBY, xwrap = (OFF)wv * VBY;
+  const OFF sj = (OFF)dr * pj + xstep, cj = pj - xwrap;
+  const OFF sp = (OFF)dr * pp + xstep, cp = pp - xwrap;
+  const OFF so = (OFF)dr * po + xstep, co = po - xwrap;
+  const OFF x0b = (OFF)R.x0 * EB + (OFF)x * VBY;
+  OFF oj = (OFF)(R.y0 + r) * pj + x0b;
+  OFF op = (OFF)(R.y0 + r) * pp + x0b;
+  OFF oo = (OFF)(R.y0 + r) * po + (OFF)x * VBY;
 
-  for (int q0 = tid; q0 < nvec; q0 += nthreads * U) {
+  // one batch: U output vectors per lane with every operand they read
+  struct Batch {
     Vec<VB> m[U], up[U], lf[U], cn[U], pm[U], pu[U], pl[U], pc[U];
     int yy[U], xx[U];
+    OFF od[U];
     bool ok[U];
+  };
+  // issue the loads of the lane's next U vectors and advance its position
+  auto issue = [&](Batch &b) {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const int q = q0 + k * nthreads;
-      ok[k] = q < nvec;
-      // row = q / wv exactly: the float quotient is within one of it for q < 2^24
-      int r = (int)((float)q * R.inv_wv);
-      r -= (r * R.wv > q) ? 1 : 0;
-      r += ((r + 1) * R.wv <= q) ? 1 : 0;
-      const int y = R.y0 + r;
-      const int x = R.x0 + (q - r * R.wv) * V;
-      yy[k] = y;
-      xx[k] = x;
-      const int64_t oj = (int64_t)y * R.pitch_j + (int64_t)x * EB;
-      const int64_t op = (int64_t)y * R.pitch_p + (int64_t)x * EB;
-      if (ok[k]) {
-        m[k] = vload<VB, SB_BLEND_NT>(R.m + oj);
-        if constexpr (HS) up[k] = vload<VB, SB_BLEND_NT>(R.u + oj);
-        if constexpr (WS) lf[k] = vload<VB, SB_BLEND_NT>(R.l + op);
-        if constexpr (HS && WS) cn[k] = vload<VB, SB_BLEND_NT>(R.c + op);
+      b.ok[k] = r < nrows;
+      b.yy[k] = R.y0 + r;
+      b.xx[k] = R.x0 + x * V;
+      b.od[k] = oo;
+      if (b.ok[k]) {
+        b.m[k] = vload<VB, SB_BLEND_NT>(R.m + oj);
+        if constexpr (HS) b.up[k] = vload<VB, SB_BLEND_NT>(R.u + oj);
+        if constexpr (WS) b.lf[k] = vload<VB, SB_BLEND_NT>(R.l + op);
+        if constexpr (HS && WS) b.cn[k] = vload<VB, SB_BLEND_NT>(R.c + op);
         if constexpr (TS) {
-          pm[k] = vload<VB, SB_BLEND_NT>(R.pm + oj);
-          if constexpr (HS) pu[k] = vload<VB, SB_BLEND_NT>(R.pu + oj);
-          if constexpr (WS) pl[k] = vload<VB, SB_BLEND_NT>(R.pl + op);
-          if constexpr (HS && WS) pc[k] = vload<VB, SB_BLEND_NT>(R.pc + op);
+          b.pm[k] = vload<VB, SB_BLEND_NT>(R.pm + oj);
+          if constexpr (HS) b.pu[k] = vload<VB, SB_BLEND_NT>(R.pu + oj);
+          if constexpr (WS) b.pl[k] = vload<VB, SB_BLEND_NT>(R.pl + op);
+          if constexpr (HS && WS) b.pc[k] = vload<VB, SB_BLEND_NT>(R.pc + op);
         }
       }
+      r += dr;
+      x += dx;
+      oj += sj;
+      op += sp;
+      oo += so;
+      if (x >= wv) {
+        x -= wv;
+        r += 1;
+        oj += cj;
+        op += cp;
+        oo += co;
+      }
     }
+  };
+  // blend the batch's vectors and store them
+  auto process = [&](Batch &b) {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      if (!ok[k]) continue;
-      char *dst = R.o + (int64_t)yy[k] * R.opitch + (int64_t)(xx[k] - R.x0) * EB;
+      if (!b.ok[k]) continue;
+      char *dst = R.o + b.od[k];
       if constexpr (!HS && !WS && !TS) {
-        vstore<VB, SB_BLEND_NT_STORE>(dst, m[k]);
+        vstore<VB, SB_BLEND_NT_STORE>(dst, b.m[k]);
       } else if constexpr (DT != DT_F32 && VB == 16) {
         // packed pairs of 16-bit elements
         constexpr int NW = Vec<VB>::NW;
         f32x2 ha, hb; // row coefficients (one per row, both lanes)
         if constexpr (HS) {
-          const float2 c = R.ch[yy[k]];
+          const float2 c = R.ch[b.yy[k]];
           ha.x = ha.y = c.x;
           hb.x = hb.y = c.y;
         }
@@ -190,7 +228,7 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
         if constexpr (WS) {
 #pragma unroll
           for (int w = 0; w < NW; ++w) {
-            const float2 c0 = R.cw[xx[k] + 2 * w], c1 = R.cw[xx[k] + 2 * w + 1];
+            const float2 c0 = R.cw[b.xx[k] + 2 * w], c1 = R.cw[b.xx[k] + 2 * w + 1];
             wa[w].x = c0.x; wa[w].y = c1.x;
             wb[w].x = c0.y; wb[w].y = c1.y;
           }
@@ -215,10 +253,10 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
           }
         };
         Vec<VB> S;
-        spatial2(m[k], up[k], lf[k], cn[k], S);
+        spatial2(b.m[k], b.up[k], b.lf[k], b.cn[k], S);
         if constexpr (TS) {
           Vec<VB> Sp;
-          spatial2(pm[k], pu[k], pl[k], pc[k], Sp);
+          spatial2(b.pm[k], b.pu[k], b.pl[k], b.pc[k], Sp);
           f32x2 ta, tb;
           ta.x = ta.y = R.ct.x;
           tb.x = tb.y = R.ct.y;
@@ -228,11 +266,11 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
         vstore<VB, SB_BLEND_NT_STORE>(dst, S);
       } else {
         float2 chh = make_float2(0.f, 0.f);
-        if constexpr (HS) chh = R.ch[yy[k]];
+        if constexpr (HS) chh = R.ch[b.yy[k]];
         float2 cww[V];
         if constexpr (WS) {
 #pragma unroll
-          for (int e = 0; e < V; ++e) cww[e] = R.cw[xx[k] + e];
+          for (int e = 0; e < V; ++e) cww[e] = R.cw[b.xx[k] + e];
         }
         // closed form of the spatial blends for one chunk
         auto spatial = [&](const Vec<VB> &vm, const Vec<VB> &vu, const Vec<VB> &vl,
@@ -264,29 +302,36 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
           }
         };
         float S[V];
-        spatial(m[k], up[k], lf[k], cn[k], S);
+        spatial(b.m[k], b.up[k], b.lf[k], b.cn[k], S);
         if constexpr (TS) {
           float Sp[V];
-          spatial(pm[k], pu[k], pl[k], pc[k], Sp);
+          spatial(b.pm[k], b.pu[k], b.pl[k], b.pc[k], Sp);
 #pragma unroll
           for (int e = 0; e < V; ++e) S[e] = crossfade<DT>(Sp[e], S[e], R.ct);
         }
         vstore<VB, SB_BLEND_NT_STORE>(dst, pack<DT, VB>(S));
       }
     }
+  };
+  Batch A;
+  while (r < nrows) {
+    issue(A);
+    process(A);
   }
 }
 
-template <int DT, int VB>
-__global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_kernel(const BlendArgs A) {
+// One work item: output frame bx of the (plane, frame) range, W segment by,
+// row band bz.  Returns whether the coefficient tables in LDS were written.
+template <int DT, int VB, class OFF>
+__device__ __forceinline__ bool blend_item(const BlendArgs &A, float2 *s_tab, uint32_t bx, uint32_t by,
+                                           uint32_t bz) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
-  extern __shared__ float2 s_tab[]; // [ew_max] column coefficients, then [rows_per_block] row ones
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int nw = A.n_w, nh = A.n_h, nt = A.n_t;
 
   // ---- W segment: tile column j, seam or body (block-uniform) ----
-  const int sw = blockIdx.y; // grid: x = (plane, frame), y = W segment, z = row band
+  const int sw = by; // x = (plane, frame), y = W segment, z = row band
   const int j = (sw + 1) >> 1;
   const bool wseam = (sw & 1) != 0;
   const int wj = A.ext[2][j];
@@ -296,10 +341,10 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_ke
   const int ews = min(ew, cw);
   const int x0 = wseam ? 0 : ews;
   const int x1 = wseam ? ews : cw;
-  if (x1 <= x0) return; // empty segment (no seam, or a tile that is all seam)
+  if (x1 <= x0) return false; // empty segment (no seam, or a tile that is all seam)
 
   // ---- frame: temporal tile tau, local frame f (block-uniform) ----
-  const uint32_t pz = blockIdx.x;
+  const uint32_t pz = bx;
   const uint32_t pli = fdiv(pz, A.div_nF);
   const int64_t plane = (int64_t)A.plane0 + pli;
   const int f_out = A.F0 + (int)(pz - pli * (uint32_t)A.nF);
@@ -312,7 +357,7 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_ke
   const int fp = tp - et + f; // frame of chunk tau-1 blended into frame f
 
   // ---- output rows of this block ----
-  const int r0 = blockIdx.z * A.rows_per_block;
+  const int r0 = (int)bz * A.rows_per_block;
   const int r1 = min(r0 + A.rows_per_block, A.nY);
   const int yo0 = A.Y0 + r0, yo1 = A.Y0 + r1;
 
@@ -393,17 +438,29 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_ke
 
     const int cls = (ts ? 4 : 0) | (hs ? 2 : 0) | (wseam ? 1 : 0);
     switch (cls) {
-      case 0: run_rows<DT, VB, false, false, false>(R, tid, nthr); break;
-      case 1: run_rows<DT, VB, false, true, false>(R, tid, nthr); break;
-      case 2: run_rows<DT, VB, true, false, false>(R, tid, nthr); break;
-      case 3: run_rows<DT, VB, true, true, false>(R, tid, nthr); break;
-      case 4: run_rows<DT, VB, false, false, true>(R, tid, nthr); break;
-      case 5: run_rows<DT, VB, false, true, true>(R, tid, nthr); break;
-      case 6: run_rows<DT, VB, true, false, true>(R, tid, nthr); break;
-      default: run_rows<DT, VB, true, true, true>(R, tid, nthr); break;
+      case 0: run_rows<DT, VB, false, false, false, OFF>(R, tid, nthr); break;
+      case 1: run_rows<DT, VB, false, true, false, OFF>(R, tid, nthr); break;
+      case 2: run_rows<DT, VB, true, false, false, OFF>(R, tid, nthr); break;
+      case 3: run_rows<DT, VB, true, true, false, OFF>(R, tid, nthr); break;
+      case 4: run_rows<DT, VB, false, false, true, OFF>(R, tid, nthr); break;
+      case 5: run_rows<DT, VB, false, true, true, OFF>(R, tid, nthr); break;
+      case 6: run_rows<DT, VB, true, false, true, OFF>(R, tid, nthr); break;
+      default: run_rows<DT, VB, true, true, true, OFF>(R, tid, nthr); break;
     }
     yo += yl1 - yl;
   }
+  return tables;
+}
+
+template <int DT, int VB, class OFF>
+__global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_kernel(const BlendArgs A) {
+  extern __shared__ float2 s_tab[]; // [ew_max] column coefficients, then [rows_per_block] row ones
+  // Blocks are dispatched in reverse: the last row band and the last frames
+  // first.  Row bands further down and later frames are the ones that meet row
+  // and frame seams (up to 8 reads per output vector), so the blocks left for
+  // the end of the grid are mostly plain copies, which shortens the drain.
+  blend_item<DT, VB, OFF>(A, s_tab, gridDim.x - 1 - blockIdx.x, gridDim.y - 1 - blockIdx.y,
+                          gridDim.z - 1 - blockIdx.z);
 }
 
 
@@ -659,19 +716,25 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) void blend_span_kernel(const Blen
 }
 } // namespace sb
 
+template <int DT, int VB>
+static void launch_blend_typed(const sb::BlendArgs &a, dim3 grid, dim3 b, size_t lds, hipStream_t st) {
+  if (a.off32) hipLaunchKernelGGL((sb::blend_stitch_kernel<DT, VB, uint32_t>), grid, b, lds, st, a);
+  else hipLaunchKernelGGL((sb::blend_stitch_kernel<DT, VB, int64_t>), grid, b, lds, st, a);
+}
+
 hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                            hipStream_t st) {
   using namespace sb;
   dim3 b(SB_BLEND_THREADS);
   if (dtype == DT_F32) {
-    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_F32, 16>), grid, b, lds, st, a);
-    else hipLaunchKernelGGL((blend_stitch_kernel<DT_F32, 4>), grid, b, lds, st, a);
+    if (vec16) launch_blend_typed<DT_F32, 16>(a, grid, b, lds, st);
+    else launch_blend_typed<DT_F32, 4>(a, grid, b, lds, st);
   } else if (dtype == DT_F16) {
-    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_F16, 16>), grid, b, lds, st, a);
-    else hipLaunchKernelGGL((blend_stitch_kernel<DT_F16, 2>), grid, b, lds, st, a);
+    if (vec16) launch_blend_typed<DT_F16, 16>(a, grid, b, lds, st);
+    else launch_blend_typed<DT_F16, 2>(a, grid, b, lds, st);
   } else {
-    if (vec16) hipLaunchKernelGGL((blend_stitch_kernel<DT_BF16, 16>), grid, b, lds, st, a);
-    else hipLaunchKernelGGL((blend_stitch_kernel<DT_BF16, 2>), grid, b, lds, st, a);
+    if (vec16) launch_blend_typed<DT_BF16, 16>(a, grid, b, lds, st);
+    else launch_blend_typed<DT_BF16, 2>(a, grid, b, lds, st);
   }
   return hipGetLastError();
 }

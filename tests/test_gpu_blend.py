@@ -213,3 +213,29 @@ def test_sixty_four_tiles_per_axis(sb):
     check(sb, w, workloads.draw_tiles(w), "64 along W")
     w2 = _wl("fp32", [24] * 63 + [9], [20], 8, 16, C=1)
     check(sb, w2, workloads.draw_tiles(w2), "64 along H")
+
+
+def test_output_band_beyond_two_gib_takes_64bit_offsets(sb):
+    # A band of output rows as tall as a tile spans more than 2^31 bytes here
+    # (2048 rows of 528448 fp16 columns), so the kernel forms its lane offsets
+    # in 64 bits instead of 32.  With a single tile row every output row
+    # depends only on the same row of each tile, so a few sampled rows are
+    # checked against the oracle run on just those rows.
+    h, R, E, n = 2048, 8256, 64, 64
+    ew = [R + E] * n
+    LW = (n - 1) * R + ew[-1]
+    assert h * LW * 2 >= 2**31
+    _say(f"[blend] 64-bit offsets: {n} tiles of [1,1,{h},{R + E}] fp16 -> [1,1,{h},{LW}]")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    tiles = [(torch.randn((1, 1, h, e), generator=g, device="cuda") * 0.5).to(torch.float16) for e in ew]
+    out = sb.vae_tile_blend_stitch([tiles], (0, 0, E), (1, h, R))
+    torch.cuda.synchronize()
+    rows = [0, 1, 777, 1500, h - 1]
+    sub = workloads.BlendWorkload("wide-rows", "fp16", 4, 1, 1, [1], [len(rows)], ew, (0, 0, E),
+                                  (1, len(rows), R), seed=0)
+    want = oracle.blend_workload(sub, [t[:, :, rows, :].cpu().numpy() for t in tiles])
+    got = out[:, :, rows, :].cpu().numpy()
+    compare.assert_bitexact(got, want, "fp16", "rows of a 2 GiB output band")
+    del tiles, out
+    torch.cuda.empty_cache()
