@@ -183,7 +183,8 @@ int vae_tile_ramp_blend(const void *const *tiles, const int64_t grid[6], const i
  *                              the last cut short by the edge.
  *     SB_LAYOUT_EDGE_ALIGNED   {t, ov}: the fewest tiles of side t whose neighbours
  *                              overlap by >= ov, origin_k = floor(k (L - t) / (n - 1));
- *                              one tile of L when L <= t.
+ *                              one tile of L when L <= t (whatever ov: a single tile
+ *                              has no neighbour); otherwise ov < t (SB_EARG).
  *     SB_LAYOUT_FEWEST_CALLS   {T, S, ov, M}: the fewest tiles, then the widest side
  *                              t <= M, with n * t <= B, the latents the stock (T, S) loop
  *                              decodes along the axis, and overlaps >= ov; spread evenly.

@@ -80,11 +80,14 @@ extern "C" int vae_tile_layout(int64_t L, int rule, const int64_t params[4], int
     }
     case SB_LAYOUT_EDGE_ALIGNED: {
       const int64_t t = params[0], ov = params[1];
-      if (t < 1 || ov < 0 || ov >= t) return sb_fail_message(SB_EARG, "need tile >= 1 and 0 <= overlap < tile");
+      if (t < 1 || ov < 0) return sb_fail_message(SB_EARG, "need tile >= 1 and overlap >= 0");
       if (L <= t) {
+        // one tile covers the canvas: there is no neighbour to overlap
         origins[0] = 0;
         extents[0] = L;
         rc = 1;
+      } else if (ov >= t) {
+        return sb_fail_message(SB_EARG, "overlap must be below the tile when several tiles are needed");
       } else {
         rc = spread(L, t, tiles_needed(L, t, ov), max_tiles, origins, extents);
       }
@@ -156,11 +159,12 @@ extern "C" int vae_tile_layout(int64_t L, int rule, const int64_t params[4], int
       } else {
         const int64_t t = T > ft ? T : ft;
         const int64_t ov = (T - S) > fov ? (T - S) : fov;
-        if (ov >= t) return sb_fail_message(SB_EARG, "floor overlap must be below the tile");
         if (L <= t) {
           origins[0] = 0;
           extents[0] = L;
           rc = 1;
+        } else if (ov >= t) {
+          return sb_fail_message(SB_EARG, "floor overlap must be below the tile when several tiles are needed");
         } else {
           rc = spread(L, t, tiles_needed(L, t, ov), max_tiles, origins, extents);
         }

@@ -164,6 +164,20 @@ def test_library_rejects_bad_parameters(sb, rule, params):
     assert ei.value.code == -1
 
 
+def test_single_tile_canvas_ignores_the_overlap(sb):
+    # a canvas no wider than the tile is one tile, whatever overlap is asked
+    # for (a lone tile has no neighbour); with several tiles an overlap that
+    # reaches the tile side is a bad parameter
+    for L, rule, p in [(8, "edge_aligned", [8, 8]), (5, "edge_aligned", [8, 20]),
+                       (2, "auto", [1, 1, 2, 2]), (64, "auto", [16, 16, 64, 64])]:
+        assert ol.layout(L, rule, p) == [(0, L)], (L, rule, p)
+        assert lib_tiles(sb, L, rule, p) == [(0, L)], (L, rule, p)
+    for L, rule, p in [(9, "edge_aligned", [8, 8]), (65, "auto", [16, 16, 64, 64])]:
+        with pytest.raises(sb.SeamBlendError) as ei:
+            sb.vae_tile_layout(L, rule, p)
+        assert ei.value.code == -1
+
+
 def test_library_rejects_a_layout_beyond_capacity(sb):
     with pytest.raises(sb.SeamBlendError) as ei:
         sb.vae_tile_layout(1000, "stock", [2, 1], max_tiles=16)

@@ -72,7 +72,8 @@ def layouts(draw):
     S = draw(st.integers(1, T))
     ov = draw(st.integers(0, max(0, T - 4)))
     M = draw(st.integers(ov + 4, ov + 250))
-    p = {"stock": [T, S], "edge_aligned": [T, ov], "fewest_calls": [T, S, ov, M],
+    ov_e = draw(st.integers(0, T + 4))  # may reach the tile side: valid only for one tile
+    p = {"stock": [T, S], "edge_aligned": [T, ov_e], "fewest_calls": [T, S, ov, M],
          "smallest_side": [ov, M],
          "auto": [T, S, draw(st.integers(1, 64)), draw(st.integers(0, 32))]}[rule]
     return L, rule, p
