@@ -10,13 +10,15 @@ Inputs are resident in HBM before timing.  Throughput is algorithmic bytes per
 second: blend = (all tile elements + all output elements) x 2 B, GroupNorm =
 3 x |x| x 2 B (two reads and one write of the two-pass method).
 
-Prints one JSON line (rank 0, N=1 only).  The oracle (plain C, all host cores)
-is timed on the same workload as the CPU baseline, and its output is compared
-with the GPU's (bit-exact blend, GroupNorm within tolerance).
+Prints one JSON line (rank 0, N=1 only).  The oracle (plain C, all host cores,
+and again on one thread) is timed on the same workload as the CPU baseline, and
+its output is compared with the GPU's (bit-exact blend, GroupNorm within
+tolerance).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -45,9 +47,23 @@ def parse():
                     help="skip the extra timing of the step captured in a HIP graph")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
                     help="repeat the oracle step until this much CPU time has been measured")
+    ap.add_argument("--cpu-single-seconds", type=float, default=5.0,
+                    help="the same on one thread (0 = skip the single-thread sample)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra rows (normalised-ramp wide-tile blend, tiled-encode blends)")
     return ap.parse_args()
+
+
+def cpu_model():
+    """The host CPU's model name, as the kernel reports it (None if unknown)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def ramp_bytes(w, elem):
@@ -295,7 +311,7 @@ def main():
     if not args.no_cpu_baseline:
         # repeat whole oracle steps until the sample holds enough CPU time
         cpu_s, reps = 0.0, 0
-        while reps == 0 or (cpu_s < args.cpu_min_seconds and reps < 100):
+        while reps == 0 or (cpu_s < args.cpu_min_seconds and reps < 1000):
             tc0 = time.perf_counter()
             want = oracle.blend_workload(bw, tiles)
             if has_gn:
@@ -320,7 +336,26 @@ def main():
         cpu = {"value": total_bytes * reps / cpu_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"{reps} full steps of the same workload (blend+stitch {bw.name}"
                          f"{' and ' + gw.name if has_gn else ''}), {cpu_s:.2f} s on {threads} threads",
-               "seconds": cpu_s, "steps": reps}
+               "seconds": cpu_s, "steps": reps, "cpu_model": cpu_model()}
+        if args.cpu_single_seconds > 0:
+            # the same oracle steps on one OpenMP thread (the oracle's own
+            # threading, set through the OpenMP runtime it links)
+            gomp = ctypes.CDLL("libgomp.so.1")
+            prev = gomp.omp_get_max_threads()
+            gomp.omp_set_num_threads(1)
+            try:
+                s1, r1 = 0.0, 0
+                while r1 == 0 or (s1 < args.cpu_single_seconds and r1 < 20):
+                    tc0 = time.perf_counter()
+                    oracle.blend_workload(bw, tiles)
+                    if has_gn:
+                        oracle.groupnorm(x_np, gw.groups, gw.eps, g_np, b_np, gw.dtype)
+                    s1 += time.perf_counter() - tc0
+                    r1 += 1
+            finally:
+                gomp.omp_set_num_threads(prev)
+            cpu["single_thread"] = {"value": total_bytes * r1 / s1 / 1e9, "unit": "GB/s", "seconds": s1,
+                                    "steps": r1}
 
     wl = {4: "video 5-D bf16 decode assembly: 75 tiles (5 temporal x 3 x 5; 17-frame 256x256, "
              "strides 12/192/192, blend 5/64/64) -> [1,3,49,480,832], plus patch GroupNorm "
