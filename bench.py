@@ -298,6 +298,8 @@ def main():
             if same:
                 traffic_rec[name] = rec_t["hbm_bytes_per_launch"]
     traffic = traffic_rec.get(f"config{args.config}-blend")
+    gn_parts = [traffic_rec.get(f"config{args.config}-gn-{k}") for k in ("stats", "norm")]
+    gn_traffic = sum(gn_parts) if all(t is not None for t in gn_parts) else None
     if extra:
         for k, r in extra.items():
             r["traffic"] = traffic_rec.get(k)
@@ -379,8 +381,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": blend_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": blend_gbs / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "blend_stitch_kernel", "launch_us": blend_avg_us},
-        "parts": {"blend": {"bytes": blend_bytes, "us": blend_avg_us, "GBps": blend_gbs},
-                  "groupnorm": {"bytes": gn_bytes, "us": gn_avg_us, "GBps": gn_gbs}},
+        "parts": {"blend": {"bytes": blend_bytes, "us": blend_avg_us, "GBps": blend_gbs, "traffic": traffic},
+                  "groupnorm": {"bytes": gn_bytes, "us": gn_avg_us, "GBps": gn_gbs, "traffic": gn_traffic}},
         "flushed": flushed,
         "graph": None if graph_ms is None else {"ms_per_step": graph_ms,
                                                  "value": total_bytes / (graph_ms * 1e-3) / 1e9},
