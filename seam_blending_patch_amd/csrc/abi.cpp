@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <numeric>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -286,7 +287,25 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
                                    : per_block;
   int64_t rows_pb = std::max<int64_t>(1, std::min<int64_t>(1024, per_block_l / block_cols));
   rows_pb = std::min<int64_t>(rows_pb, Ah.L);
-  {
+  // Bands that start on every tile-row and row-seam boundary hold one run
+  // each (one row class, whole batches): every such boundary is a multiple of
+  // g = gcd(R_h, e_h(1), ..., e_h(n-1)) rows from a tile row's origin, so a
+  // band height dividing g keeps them all on band edges.  Taken when a divisor
+  // of g comes within a factor of 3 of the size-based height (measured on the
+  // video workload: 64-row bands 68.6 us against 69.7 us for 60-row ones);
+  // otherwise the bands are balanced over the rows.
+  int64_t g = Ah.R;
+  for (int64_t k = 1; k < Ah.n; ++k)
+    if (Ah.e[k] > 0) g = std::gcd(g, Ah.e[k]);
+  int64_t aligned_rows = 1;
+  for (int64_t d = 1; d * d <= g; ++d)
+    if (g % d == 0) {
+      if (d <= rows_pb) aligned_rows = std::max(aligned_rows, d);
+      if (g / d <= rows_pb) aligned_rows = std::max(aligned_rows, g / d);
+    }
+  if (!span && Ah.n > 1 && aligned_rows * 3 >= rows_pb) {
+    rows_pb = aligned_rows;
+  } else {
     const int64_t nrb = (Ah.L + rows_pb - 1) / rows_pb;
     rows_pb = (Ah.L + nrb - 1) / nrb;
   }
