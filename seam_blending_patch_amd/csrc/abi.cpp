@@ -235,7 +235,8 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   // coefficient tables, a barrier), so blocks are made as large as the
   // problem allows while still giving every CU several blocks: about
   // total / (cus * SB_BLEND_BLOCKS_PER_CU) vectors in the widest W segment,
-  // clamped to [1024, 8192], then balanced over the rows.
+  // clamped to [1024, 8192]; the band height is then aligned to the row seams
+  // or balanced over the rows (below).
 #ifndef SB_BLEND_BLOCKS_PER_CU
 #define SB_BLEND_BLOCKS_PER_CU 12
 #endif
