@@ -112,7 +112,8 @@ size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape, int64_t g
 /*
  * GroupNorm of x viewed as n_patches patches along split_axis.
  *   x            device pointer, contiguous [N, C, spatial...] of dtype, ndim 3..5.
- *   shape        host array of ndim extents; C % groups == 0.
+ *   shape        host array of ndim extents; C % groups == 0; N*C <= 65535
+ *                (else SB_EGEOM).
  *   split_axis   2 <= split_axis < ndim: the spatial axis the patches cut.
  *   n_patches    1..64.  Patch p covers [s_p, s_p + len_p) along split_axis
  *                with the first (L mod P) patches one longer (empty patches

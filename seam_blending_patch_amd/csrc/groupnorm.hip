@@ -21,12 +21,13 @@
 //   first across the wavefront with shuffles, then across the 4 waves in LDS.
 //   One fp32 partial (count, m, M2, K_g) per block goes to the workspace.
 // Pass 2 (gn_norm_kernel): one block per (n, c) plane chunk.  Every wave
-//   issues its loads of x first, then merges the P x CPP partials of its group
-//   with a fixed shuffle tree (chunks of a patch first, then patches) -- the
+//   requests the P x CPP partials of its group, gamma, beta and its vectors
+//   of x, and merges the partials with a fixed shuffle tree (chunks of a patch first, then patches) -- the
 //   same order in every block, so results are deterministic -- and streams
 //   y = ((x - K_g) - m) * (rstd * gamma_c) + beta_c back out with nontemporal
-//   stores.  K_g comes from the workspace, not from x, so out may alias x.  Wave 0 of the first block of each group writes the optional
-//   per-patch statistics.
+//   stores.  K_g comes from the workspace, not from x, so out may alias x.
+//   Wave 0 of the first block of each group writes the optional per-patch
+//   statistics.
 
 #include "sb_internal.h"
 #include "sb_vec.h"
@@ -97,14 +98,10 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
   const char *gbase = (const char *)A.x +
                       (((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S + (int64_t)start * A.inner) * EB;
 
-  // the group shift K_g: the group's first element (a uniform scalar load)
-  const int64_t g0 = ((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S;
-  const float K = widen<DT>(DT == DT_F32 ? ((const uint32_t *)A.x)[g0] : ((const uint16_t *)A.x)[g0]);
   // Vectors q0 + tid + k * blockDim.x, in batches of kStatsBatch whose loads
   // are issued together.
-  float s1 = 0.f, s2 = 0.f, cnt = 0.f;
-  for (uint32_t base = q0 + tid; base < q1; base += blockDim.x * kStatsBatch) {
-    Vec<VB> v[kStatsBatch];
+  Vec<VB> v[kStatsBatch];
+  auto load_batch = [&](uint32_t base) {
 #pragma unroll
     for (int u = 0; u < kStatsBatch; ++u) {
       const uint32_t q = base + u * blockDim.x;
@@ -114,6 +111,9 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
         v[u] = vload<VB, false>(gbase + ((int64_t)r * row + (int64_t)pos * V) * EB);
       }
     }
+  };
+  float s1 = 0.f, s2 = 0.f, cnt = 0.f;
+  auto accumulate = [&](uint32_t base, float K) {
 #pragma unroll
     for (int u = 0; u < kStatsBatch; ++u) {
       if (base + u * blockDim.x < q1) {
@@ -128,6 +128,19 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
         cnt += (float)V;
       }
     }
+  };
+  // The first batch is issued before the group shift K_g (the group's first
+  // element) is read, so the two share one memory latency; every later batch
+  // finds K_g in a register.
+  const uint32_t step = blockDim.x * kStatsBatch;
+  uint32_t base = q0 + tid;
+  load_batch(base);
+  const int64_t g0 = ((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S;
+  const float K = widen<DT>(DT == DT_F32 ? ((const uint32_t *)A.x)[g0] : ((const uint16_t *)A.x)[g0]);
+  accumulate(base, K);
+  for (base += step; base < q1; base += step) {
+    load_batch(base);
+    accumulate(base, K);
   }
   Stat st;
   st.n = cnt;
@@ -157,46 +170,66 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
   }
 }
 
-constexpr int kNormUnroll = 4;
+template <int DT> __device__ __forceinline__ uint32_t load_elem(const void *p, int64_t i) {
+  return DT == DT_F32 ? ((const uint32_t *)p)[i] : (uint32_t)((const uint16_t *)p)[i];
+}
 
-template <int DT, int VB>
+template <int DT, int VB, bool XFIRST>
 __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
-  const int64_t plane = blockIdx.y;
-  const int n = (int)(plane / A.C);
-  const int ch = (int)(plane - (int64_t)n * A.C);
-  const int g = ch / A.Cg;
+  const uint32_t plane = blockIdx.y; // < 2^16
+  const int n = (int)fdiv(plane, A.div_C);
+  const int ch = (int)(plane - (uint32_t)n * (uint32_t)A.C);
+  const int g = (int)fdiv((uint32_t)ch, A.div_Cg);
   const int64_t Sv = A.S / V;
   const int64_t q0 = (int64_t)chunk * A.per2;
   const int64_t q1 = min(q0 + A.per2, Sv);
-  const char *xb = (const char *)A.x + plane * A.S * EB;
-  char *yb = (char *)A.out + plane * A.S * EB;
+  const char *xb = (const char *)A.x + (int64_t)plane * A.S * EB;
+  char *yb = (char *)A.out + (int64_t)plane * A.S * EB;
 
-  // loads first, so their latency overlaps the statistics merge
-  Vec<VB> xs[kNormUnroll];
-#pragma unroll
-  for (int u = 0; u < kNormUnroll; ++u) {
-    const int64_t q = q0 + (int64_t)u * blockDim.x + tid;
-    if (q < q1) xs[u] = vload<VB, SB_GN_NT_LOAD2>(xb + q * V * EB);
-  }
-
-  // merge the group's partials: lane l holds (patch l / CPP, chunk l % CPP)
+  // The group's partials (lane l holds patch l / CPP, chunk l % CPP), this
+  // channel's gamma and beta, and the block's vectors of x.  gamma and beta
+  // are read unconditionally (from x when absent) and x at a clamped index, so
+  // no load sits behind a branch.  Small grids (one or two waves of blocks
+  // over the chip) request x first, so HBM starts streaming at once; large
+  // grids request the small loads first, and the merge below waits for them
+  // alone while x is in flight (measured: each order is the faster one on its
+  // side of the threshold the host sets).
   const int lane = tid & 63;
   const int K = A.P * A.CPP;
-  Stat st{0.f, 0.f, 0.f};
-  float kg = 0.f; // the group shift K_g (the same in every partial of the group)
-  if (lane < K) {
-    const float4 src = reinterpret_cast<const float4 *>(A.part)[(int64_t)(n * A.G + g) * K + lane];
-    st.n = src.x;
-    st.mean = src.y;
-    st.m2 = src.z;
-    kg = src.w;
+  float4 src = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint32_t graw, braw;
+  Vec<VB> xs[kNormUnroll];
+  auto load_small = [&]() {
+    if (lane < K) src = reinterpret_cast<const float4 *>(A.part)[(int64_t)(n * A.G + g) * K + lane];
+    graw = load_elem<DT>(A.gamma ? A.gamma : A.x, A.gamma ? ch : 0);
+    braw = load_elem<DT>(A.beta ? A.beta : A.x, A.beta ? ch : 0);
+  };
+  auto load_x = [&]() {
+#pragma unroll
+    for (int u = 0; u < kNormUnroll; ++u) {
+      const int64_t q = min(q0 + (int64_t)u * blockDim.x + tid, q1 - 1); // q1 > q0: the plane is non-empty
+      xs[u] = vload<VB, SB_GN_NT_LOAD2>(xb + q * V * EB);
+    }
+  };
+  if constexpr (XFIRST) {
+    load_x();
+    load_small();
+  } else {
+    load_small();
+    load_x();
   }
+  const float gam = A.gamma ? widen<DT>(graw) : 1.0f;
+  const float bet = A.beta ? widen<DT>(braw) : 0.0f;
+
+  // merge the group's partials
+  Stat st{src.x, src.y, src.z};
+  const float kg = src.w; // the group shift K_g (the same in every partial of the group)
   const float Kg = __shfl(kg, 0, 64);
-  const bool writer = A.patch_stats != nullptr && chunk == 0 && (ch % A.Cg) == 0 && tid < 64;
+  const bool writer = A.patch_stats != nullptr && chunk == 0 && ch == g * A.Cg && tid < 64;
   if (writer && A.CPP == 1 && lane < A.P) {
     float *d = A.patch_stats + ((int64_t)(n * A.G + g) * A.P + lane) * 3;
     d[0] = st.n; d[1] = st.n > 0.f ? Kg + st.mean : 0.f; d[2] = st.m2;
@@ -215,12 +248,6 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   const float m2 = __shfl(st.m2, 0, 64);
   const float var = m2 / cnt;
   const float rstd = 1.0f / sqrtf(var + A.eps);
-  const float gam = A.gamma ? widen<DT>(DT == DT_F32 ? ((const uint32_t *)A.gamma)[ch]
-                                                     : ((const uint16_t *)A.gamma)[ch])
-                            : 1.0f;
-  const float bet = A.beta ? widen<DT>(DT == DT_F32 ? ((const uint32_t *)A.beta)[ch]
-                                                    : ((const uint16_t *)A.beta)[ch])
-                           : 0.0f;
   const float a = rstd * gam;
 
 #pragma unroll
@@ -247,8 +274,11 @@ static hipError_t launch_gn(const GNArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((gn_stats_kernel<DT, VB>), dim3(blocks1), dim3(256), 0, st, a, db, ds);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gn_norm_kernel<DT, VB>), dim3((unsigned)a.chunks2, (unsigned)((int64_t)a.N * a.C)),
-                     dim3(256), 0, st, a);
+  const dim3 grid2((unsigned)a.chunks2, (unsigned)((int64_t)a.N * a.C));
+  if (a.x_first)
+    hipLaunchKernelGGL((gn_norm_kernel<DT, VB, true>), grid2, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gn_norm_kernel<DT, VB, false>), grid2, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -70,6 +70,10 @@ struct SpanCol {
 // GroupNorm launch arguments
 // ---------------------------------------------------------------------------
 constexpr int kMaxPatches = 64;
+#ifndef SB_GN_NORM_UNROLL
+#define SB_GN_NORM_UNROLL 4
+#endif
+constexpr int kNormUnroll = SB_GN_NORM_UNROLL; // vectors per thread in the normalise pass
 
 struct GNArgs {
   const void *x;
@@ -89,6 +93,8 @@ struct GNArgs {
   // pass 2
   int32_t chunks2;    // blocks per (n, c) plane
   int64_t per2;       // vectors per pass-2 block
+  FastDiv div_C, div_Cg; // plane -> (n, c) and channel -> group
+  int32_t x_first;    // pass 2 requests x before the partials (small grids)
 };
 
 // ---------------------------------------------------------------------------

@@ -100,7 +100,8 @@ def test_groupnorm_workspace_and_validation(sb):
                               ((1, 32, 8, 8), 4, 4, 2),   # axis out of range
                               ((1, 32, 8, 8), 4, 2, 0),   # no patches
                               ((1, 32, 8, 8), 4, 2, 65),  # too many patches
-                              ((1, 32), 4, 2, 1)]:        # rank
+                              ((1, 32), 4, 2, 1),         # rank
+                              ((2, 40000, 4, 8), 8, 2, 1)]:  # N*C above 65535 planes
         with pytest.raises(sb.SeamBlendError):
             sb.patch_groupnorm_workspace_bytes(shape, G, axis, P)
 

@@ -82,6 +82,7 @@ CASES = [
     ((1, 8, 64, 64), 2, 3, 64),      # the maximum patch count
     ((2, 4, 100), 2, 2, 3),          # 3-D
     ((1, 64, 40, 40), 32, 2, 1),     # a single patch
+    ((1, 8192, 16, 16), 64, 2, 3),   # 8192 normalise blocks: the large-grid load order
 ]
 
 
