@@ -51,6 +51,10 @@ def parse():
                     help="the same on one thread (0 = skip the single-thread sample)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra rows (normalised-ramp wide-tile blend, tiled-encode blends)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE output of two "
+                         "'--steps 3 --warmup 1 --no-cpu-baseline --flushed-reps 0 --copy-calibration "
+                         "--no-graph' runs and write profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -84,6 +88,111 @@ def ramp_bytes(w, elem):
         planes *= v
     LH, LW = w.out_shape[-2:]
     return planes * (sum(ch) * sum(cw) + LH * LW) * elem
+
+
+RAMP_NAMES = ("qwen21-2048-bf16", "qwen21-2752x1536-bf16", "flux-1600-bf16", "qwen21-encode-2048-bf16")
+KERNEL_SOURCES = {
+    "blend": ["seam_blending_patch_amd/csrc/blend_stitch.hip", "seam_blending_patch_amd/csrc/abi.cpp"],
+    "gn": ["seam_blending_patch_amd/csrc/groupnorm.hip", "seam_blending_patch_amd/csrc/abi.cpp"],
+    "ramp": ["seam_blending_patch_amd/csrc/ramp_blend.hip", "seam_blending_patch_amd/csrc/ramp.cpp"],
+}
+COMMON_SOURCES = ["seam_blending_patch_amd/csrc/sb_internal.h", "seam_blending_patch_amd/csrc/sb_vec.h"]
+
+
+def blend_out_elems(w):
+    """Output elements of a stock blend + stitch: per axis (n - 1) * R + last extent."""
+    L = [(len(e) - 1) * r + e[-1] for e, r in zip((w.ext_t, w.ext_h, w.ext_w), w.row_limit)]
+    return w.N * w.C * L[0] * L[1] * L[2]
+
+
+def write_traffic(fetch_dir, write_dir, config, path=None):
+    """profiles/traffic.json from two rocprofv3 --pmc runs of this benchmark
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Dispatches are grouped by
+    (kernel, grid); the library's groups appear in the order the benchmark
+    launches them (the step's blend, the two GroupNorm passes, then the extra
+    rows), and the device copy of 256 MiB that --copy-calibration runs gives
+    the scale from each counter to bytes."""
+    import csv
+    import glob
+
+    import numpy as np
+
+    import workloads
+
+    def groups(d):
+        paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if len(paths) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {d}, found {paths}")
+        order, vals = [], {}
+        rows = sorted(csv.DictReader(open(paths[0])), key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
+            gk = tuple(r[k] for k in sorted(r) if k.startswith("Grid_Size"))
+            key = (r["Kernel_Name"], gk)
+            if key not in vals:
+                order.append(key)
+                vals[key] = {}
+            disp = vals[key].setdefault(r["Dispatch_Id"], 0.0)
+            vals[key][r["Dispatch_Id"]] = disp + float(r["Counter_Value"])
+        return [(k, sum(vals[k].values()) / len(vals[k]), len(vals[k])) for k in order]
+
+    def split(gs):
+        ours = [g for g in gs if "sb::" in g[0][0]]
+        copy = [g for g in gs if "copyBuffer" in g[0][0]]
+        if not copy:
+            raise SystemExit("no device copy kernel in the counter run (run it with --copy-calibration)")
+        return ours, max(copy, key=lambda g: g[1])
+
+    fo, fc = split(groups(fetch_dir))
+    wo, wc = split(groups(write_dir))
+    cal_bytes = 256 << 20
+    fscale, wscale = cal_bytes / (fc[1] * 1024), cal_bytes / (wc[1] * 1024)
+    cfg = workloads.CONFIGS[config]
+    bw, gw = cfg.blend, cfg.groupnorm
+    eb = workloads.ITEMSIZE[bw.dtype]
+    names = [(f"config{config}-blend", "blend", (bw.tile_elems() + blend_out_elems(bw)) * eb)]
+    if gw is not None:
+        n = int(np.prod(gw.shape)) * workloads.ITEMSIZE[gw.dtype]
+        names += [(f"config{config}-gn-stats", "gn", n), (f"config{config}-gn-norm", "gn", 2 * n)]
+    for name in RAMP_NAMES:
+        rw = workloads.RAMP_WORKLOADS[name]
+        names.append(("ramp:" + name, "ramp", ramp_bytes(rw, workloads.ITEMSIZE[rw.dtype])))
+    for name, ew in workloads.ENCODE_BLEND_WORKLOADS.items():
+        names.append(("encode-blend:" + name, "blend",
+                      (ew.tile_elems() + blend_out_elems(ew)) * workloads.ITEMSIZE[ew.dtype]))
+    if len(fo) != len(names) or len(wo) != len(names) or [g[0] for g in fo] != [g[0] for g in wo]:
+        raise SystemExit(f"{len(fo)} / {len(wo)} launch groups in the counter runs, {len(names)} expected")
+
+    def sha(f):
+        return hashlib.sha256(open(os.path.join(ROOT, f), "rb").read()).hexdigest()
+
+    launches = {}
+    for (name, part, alg), f, w in zip(names, fo, wo):
+        hbm = f[1] * 1024 * fscale + w[1] * 1024 * wscale
+        launches[name] = {"kernel": f[0][0], "grid": list(f[0][1]), "dispatches": f[2],
+                          "sources_sha256": {s_: sha(s_) for s_ in KERNEL_SOURCES[part] + COMMON_SOURCES},
+                          "fetch_kib_per_dispatch": f[1], "write_kib_per_dispatch": w[1],
+                          "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg,
+                          "excess": hbm / alg - 1.0}
+    cmd = ("python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline --flushed-reps 0 "
+           "--copy-calibration --no-graph")
+    rec = {"what": "HBM bytes per launch from rocprofv3 PMC counters FETCH_SIZE and WRITE_SIZE (KiB per "
+                   "dispatch), each scaled by what the counter reads for a plain 256 MiB device copy "
+                   "(__amd_rocclr_copyBuffer) in the same run",
+           "calibration": {"bytes_read": cal_bytes, "bytes_written": cal_bytes, "fetch_kib": fc[1],
+                           "write_kib": wc[1], "fetch_scale": fscale, "write_scale": wscale},
+           "commands": ["cd /tmp && export TMPDIR=/tmp",
+                        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o run -- {cmd}",
+                        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o run -- {cmd}",
+                        "python3 $REPO/bench.py --traffic-from $REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write"],
+           "launches": launches}
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    for name, r in launches.items():
+        print(f"{name:40s} {r['hbm_bytes_per_launch']:14.0f} B  algorithmic {r['algorithmic_bytes_per_launch']:12d}"
+              f"  {100 * r['excess']:+.1f}%  ({r['kernel'][:40]})")
+    return path
 
 
 def time_launches(torch, call, nbytes, steps, warmup, flushed_reps, dev):
@@ -124,6 +233,9 @@ def time_launches(torch, call, nbytes, steps, warmup, flushed_reps, dev):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.config)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
@@ -257,7 +369,7 @@ def main():
     extra = None
     if not args.no_extra:
         extra = {}
-        for name in ("qwen21-2048-bf16", "qwen21-2752x1536-bf16", "flux-1600-bf16", "qwen21-encode-2048-bf16"):
+        for name in RAMP_NAMES:
             rw = workloads.RAMP_WORKLOADS[name]
             rt = workloads.draw_ramp_tiles(rw)
             nw_ = len(rw.origins_w)

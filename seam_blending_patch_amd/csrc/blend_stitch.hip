@@ -330,36 +330,60 @@ __device__ __forceinline__ bool blend_item(const BlendArgs &A, float2 *s_tab, ui
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int nw = A.n_w, nh = A.n_h, nt = A.n_t;
 
-  // ---- W segment: tile column j, seam or body (block-uniform) ----
+  // ---- block-uniform indices: arithmetic on the block index and the fixed
+  //      argument fields only ----
   const int sw = by; // x = (plane, frame), y = W segment, z = row band
   const int j = (sw + 1) >> 1;
   const bool wseam = (sw & 1) != 0;
-  const int wj = A.ext[2][j];
-  const int wp = j > 0 ? A.ext[2][j - 1] : 0;
-  const int ew = j > 0 ? min(A.E[2], min(wp, wj)) : 0;
-  const int cw = j < nw - 1 ? A.R[2] : wj;
-  const int ews = min(ew, cw);
-  const int x0 = wseam ? 0 : ews;
-  const int x1 = wseam ? ews : cw;
-  if (x1 <= x0) return false; // empty segment (no seam, or a tile that is all seam)
-
-  // ---- frame: temporal tile tau, local frame f (block-uniform) ----
   const uint32_t pz = bx;
   const uint32_t pli = fdiv(pz, A.div_nF);
   const int64_t plane = (int64_t)A.plane0 + pli;
   const int f_out = A.F0 + (int)(pz - pli * (uint32_t)A.nF);
   const int tau = min((int)fdiv((uint32_t)f_out, A.div_Rt), nt - 1);
   const int f = f_out - tau * A.R[0];
-  const int tt = A.ext[0][tau];
-  const int tp = tau > 0 ? A.ext[0][tau - 1] : 0;
+  const int r0 = (int)bz * A.rows_per_block;
+  const int r1 = min(r0 + A.rows_per_block, A.nY);
+  const int yo0 = A.Y0 + r0, yo1 = A.Y0 + r1;
+  const int ia = min((int)fdiv((uint32_t)yo0, A.div_Rh), nh - 1); // tile row of the first run
+
+  // ---- the extents and tile pointers of the block's first run, all requested
+  //      at once: every index is clamped into the launch window (tau-1 and
+  //      i-1 never fall below the window's first chunk and tile row), so the
+  //      loads need no branch and share one memory latency; the ones a block
+  //      has no seam for are simply not used ----
+  const int jm = max(j - 1, 0), taum = max(tau - 1, 0), iam = max(ia - 1, 0);
+  const int wj = A.ext[2][j], wjm = A.ext[2][jm];
+  const int tt = A.ext[0][tau], ttm = A.ext[0][taum];
+  const int hia = A.ext[1][ia], hiam = A.ext[1][iam];
+  const char *const *P = (const char *const *)A.ptr;
+  auto tile = [&](int tq, int ti, int tj) {
+    return P[((tq - A.taub) * A.ptr_nh + (ti - A.ib)) * nw + tj];
+  };
+  struct Tiles {
+    const char *m, *u, *l, *c, *pm, *pu, *pl, *pc;
+  };
+  auto tiles_of_row = [&](int i) {
+    const int im = max(i - 1, 0);
+    return Tiles{tile(tau, i, j),     tile(tau, im, j),     tile(tau, i, jm),     tile(tau, im, jm),
+                 tile(taum, i, j),    tile(taum, im, j),    tile(taum, i, jm),    tile(taum, im, jm)};
+  };
+  Tiles T = tiles_of_row(ia);
+
+  // ---- W segment: tile column j, seam or body ----
+  const int wp = j > 0 ? wjm : 0;
+  const int ew = j > 0 ? min(A.E[2], min(wp, wj)) : 0;
+  const int cw = j < nw - 1 ? A.R[2] : wj;
+  const int ews = min(ew, cw);
+  const int x0 = wseam ? 0 : ews;
+  const int x1 = wseam ? ews : cw;
+
+  // ---- frame: temporal tile tau, local frame f ----
+  const int tp = tau > 0 ? ttm : 0;
   const int et = tau > 0 ? min(A.E[0], min(tp, tt)) : 0;
   const bool ts = f < et;
   const int fp = tp - et + f; // frame of chunk tau-1 blended into frame f
 
-  // ---- output rows of this block ----
-  const int r0 = (int)bz * A.rows_per_block;
-  const int r1 = min(r0 + A.rows_per_block, A.nY);
-  const int yo0 = A.Y0 + r0, yo1 = A.Y0 + r1;
+  if (x1 <= x0) return false; // empty segment (no seam, or a tile that is all seam)
 
   // ---- coefficient tables (only the ones this block's seams use) ----
   float2 *s_cw = s_tab;
@@ -368,37 +392,39 @@ __device__ __forceinline__ bool blend_item(const BlendArgs &A, float2 *s_tab, ui
   if (wseam)
     for (int x = tid; x < ews; x += nthr) s_cw[x] = coefficients(x, ew);
   if (A.E[1] > 0) {
-    // does the row band meet a row seam?  (block-uniform)
-    const int ia = min((int)fdiv((uint32_t)yo0, A.div_Rh), nh - 1);
+    // the seam rows of each tile row the band meets (block-uniform loop; a
+    // band aligned to the row seams meets one tile row)
     const int ib2 = min((int)fdiv((uint32_t)(yo1 - 1), A.div_Rh), nh - 1);
-    const int ylo = yo0 - ia * A.R[1];
-    const bool meets = ib2 > ia || (ia > 0 && ylo < min(A.E[1], min(A.ext[1][ia - 1], A.ext[1][ia])));
-    if (meets) {
-      tables = true;
-      for (int k = tid; k < r1 - r0; k += nthr) {
-        const int yo = yo0 + k;
-        const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
-        const int y = yo - i * A.R[1];
-        const int eh = i > 0 ? min(A.E[1], min(A.ext[1][i - 1], A.ext[1][i])) : 0;
-        if (y < eh) s_ch[k] = coefficients(y, eh);
+    int hi = hia, hp = hiam;
+    for (int i = ia;;) {
+      const int eh = i > 0 ? min(A.E[1], min(hp, hi)) : 0;
+      const int ybase = i * A.R[1];
+      const int lo = max(yo0, ybase), hi_row = min(yo1, ybase + eh);
+      if (hi_row > lo) {
+        tables = true;
+        for (int k = lo - yo0 + tid; k < hi_row - yo0; k += nthr) s_ch[k] = coefficients(yo0 + k - ybase, eh);
       }
+      if (++i > ib2) break;
+      hp = hi;
+      hi = A.ext[1][i];
     }
   }
   const float2 ct = ts ? coefficients(f, et) : make_float2(0.f, 0.f);
   if (tables) __syncthreads();
 
-  const char *const *P = (const char *const *)A.ptr;
-  auto tile = [&](int tq, int ti, int tj) {
-    return P[((tq - A.taub) * A.ptr_nh + (ti - A.ib)) * nw + tj];
-  };
-
   // ---- runs of rows with one tile row and one row class ----
+  int cur = ia;                // tile row whose extents and tiles are loaded
+  int hi = hia, hp = hiam;     // its extent and the one above (clamped at row 0)
   int yo = yo0;
   while (yo < yo1) {
     const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
+    if (i != cur) { // the band crosses into the next tile row
+      cur = i;
+      hp = A.ext[1][i - 1];
+      hi = A.ext[1][i];
+      T = tiles_of_row(i);
+    }
     const int ybase = i * A.R[1];
-    const int hi = A.ext[1][i];
-    const int hp = i > 0 ? A.ext[1][i - 1] : 0;
     const int eh = i > 0 ? min(A.E[1], min(hp, hi)) : 0;
     const int chh = i < nh - 1 ? A.R[1] : hi;
     const int ehs = min(eh, chh);
@@ -412,17 +438,16 @@ __device__ __forceinline__ bool blend_item(const BlendArgs &A, float2 *s_tab, ui
     const int64_t pj = (int64_t)wj * EB, pp = (int64_t)wp * EB;
     R.pitch_j = pj;
     R.pitch_p = pp;
-    R.m = tile(tau, i, j) + ((plane * tt + f) * hi) * pj;
+    R.m = T.m + ((plane * tt + f) * hi) * pj;
     R.u = R.l = R.c = R.pm = R.pu = R.pl = R.pc = nullptr;
-    if (hs) R.u = tile(tau, i - 1, j) + ((plane * tt + f) * hp + u) * pj;
-    if (wseam) R.l = tile(tau, i, j - 1) + ((plane * tt + f) * hi) * pp + (int64_t)l * EB;
-    if (hs && wseam) R.c = tile(tau, i - 1, j - 1) + ((plane * tt + f) * hp + u) * pp + (int64_t)l * EB;
+    if (hs) R.u = T.u + ((plane * tt + f) * hp + u) * pj;
+    if (wseam) R.l = T.l + ((plane * tt + f) * hi) * pp + (int64_t)l * EB;
+    if (hs && wseam) R.c = T.c + ((plane * tt + f) * hp + u) * pp + (int64_t)l * EB;
     if (ts) {
-      R.pm = tile(tau - 1, i, j) + ((plane * tp + fp) * hi) * pj;
-      if (hs) R.pu = tile(tau - 1, i - 1, j) + ((plane * tp + fp) * hp + u) * pj;
-      if (wseam) R.pl = tile(tau - 1, i, j - 1) + ((plane * tp + fp) * hi) * pp + (int64_t)l * EB;
-      if (hs && wseam)
-        R.pc = tile(tau - 1, i - 1, j - 1) + ((plane * tp + fp) * hp + u) * pp + (int64_t)l * EB;
+      R.pm = T.pm + ((plane * tp + fp) * hi) * pj;
+      if (hs) R.pu = T.pu + ((plane * tp + fp) * hp + u) * pj;
+      if (wseam) R.pl = T.pl + ((plane * tp + fp) * hi) * pp + (int64_t)l * EB;
+      if (hs && wseam) R.pc = T.pc + ((plane * tp + fp) * hp + u) * pp + (int64_t)l * EB;
     }
     R.opitch = (int64_t)A.LW * EB;
     R.o = (char *)A.out + (((plane * A.LT + f_out) * A.LH + ybase) * (int64_t)A.LW +

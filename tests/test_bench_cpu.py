@@ -72,3 +72,54 @@ def test_ramp_bytes_equal_a_brute_force_count(name):
     planes = int(np.prod(w.lead))
     LH, LW = w.out_shape[-2:]
     assert bench.ramp_bytes(w, 2) == planes * (ch * cw + LH * LW) * 2
+
+
+def _counter_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Grid_Size_X,Grid_Size_Y,Counter_Name,Counter_Value\n")
+        for r in rows:
+            f.write(",".join(str(v) for v in r) + "\n")
+
+
+def test_traffic_record_from_counter_runs(tmp_path):
+    """Dispatches grouped by (kernel, grid) in launch order, averaged per
+    dispatch, scaled by the 256 MiB copy, and matched to the benchmark's
+    launches; the file records the sources' hashes."""
+    bench = _bench_module()
+    cfg = workloads.CONFIGS[4]
+    n_extra = len(bench.RAMP_NAMES) + len(workloads.ENCODE_BLEND_WORKLOADS)
+    kernels = ([("sb::blend_stitch_kernel", 1), ("sb::gn_stats_kernel", 2), ("sb::gn_norm_kernel", 3)]
+               + [(f"sb::extra_{k}", 10 + k) for k in range(n_extra)])
+    for counter, scale in (("FETCH_SIZE", 0.5), ("WRITE_SIZE", 1.0)):
+        rows, d = [], 0
+        for rep in range(2):  # two dispatches of every launch, values 100 and 300 KiB
+            for name, grid in kernels:
+                d += 1
+                # a counter split over two instances of the same dispatch is summed
+                rows += [(d, name, grid, 1, counter, (100 + 200 * rep) / 2),
+                         (d, name, grid, 1, counter, (100 + 200 * rep) / 2)]
+            d += 1
+            rows.append((d, "__amd_rocclr_copyBuffer", 99, 1, counter, 262144 * scale))
+        rows.append((d + 1, "torch_fill", 7, 1, counter, 5.0))
+        _counter_csv(str(tmp_path / counter / "run" / "run_counter_collection.csv"), rows)
+    out = tmp_path / "traffic.json"
+    bench.write_traffic(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"), 4, path=str(out))
+    rec = json.load(open(out))
+    assert rec["calibration"]["fetch_scale"] == pytest.approx(2.0)
+    assert rec["calibration"]["write_scale"] == pytest.approx(1.0)
+    names = list(rec["launches"])
+    assert names[:3] == ["config4-blend", "config4-gn-stats", "config4-gn-norm"]
+    assert len(names) == 3 + n_extra
+    blend = rec["launches"]["config4-blend"]
+    assert blend["dispatches"] == 2
+    assert blend["fetch_kib_per_dispatch"] == pytest.approx(200.0)
+    assert blend["hbm_bytes_per_launch"] == pytest.approx(200 * 1024 * 2.0 + 200 * 1024)
+    w = cfg.blend
+    out_elems = w.N * w.C * 49 * 480 * 832
+    assert blend["algorithmic_bytes_per_launch"] == (w.tile_elems() + out_elems) * 2
+    gn = cfg.groupnorm
+    assert rec["launches"]["config4-gn-norm"]["algorithmic_bytes_per_launch"] == 2 * 2 * int(np.prod(gn.shape))
+    for r in rec["launches"].values():
+        for f, h in r["sources_sha256"].items():
+            assert os.path.exists(os.path.join(ROOT, f)) and len(h) == 64
