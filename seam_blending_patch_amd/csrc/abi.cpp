@@ -427,6 +427,9 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
             ((int64_t)a.len_small * inner) % V16 == 0 &&
             (a.n_big == 0 || ((int64_t)a.len_big * inner) % V16 == 0);
   const int V = P.vec16 ? V16 : 1;
+  // patches across the innermost axis: pass 1 reads whole rows of at most
+  // 1024 vectors, one lane per column (see gn_stats_rows_kernel)
+  a.rows_layout = (inner == 1 && a.L / V >= 1 && a.L / V <= 1024) ? 1 : 0;
   const int64_t group_vec = (int64_t)a.Cg * S / V;
   if (group_vec >= ((int64_t)1 << 31)) return fail(SB_EGEOM, "a group exceeds 2^31 vectors");
   if (S / V >= ((int64_t)1 << 40)) return fail(SB_EGEOM, "plane too large");

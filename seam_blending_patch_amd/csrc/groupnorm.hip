@@ -174,6 +174,122 @@ template <int DT> __device__ __forceinline__ uint32_t load_elem(const void *p, i
   return DT == DT_F32 ? ((const uint32_t *)p)[i] : (uint32_t)((const uint16_t *)p)[i];
 }
 
+// Pass 1 when the patches cut the innermost axis (a W split): a patch run is
+// then only a few vectors of each row, and reading it block by block touches
+// every row of the group once per patch.  Here a block of kRowsThreads lanes
+// covers whole rows instead: lane t keeps one column of the row (t mod the
+// row's width in vectors) for the whole block, so each wave reads contiguous
+// rows and each lane accumulates for one fixed patch.  The block's lanes are
+// then merged by a fixed tree, first across the rows it read (same column),
+// then across the columns of each patch, and the block writes one partial per
+// patch: chunk c of every patch.  Same partial layout and merge order in pass 2.
+constexpr int kRowsThreads = 1024;
+
+// first element column of patch p along the split axis, and its length
+__device__ __forceinline__ int patch_start(int p, const GNArgs &A) {
+  return p < A.n_big ? p * A.len_big : A.n_big * A.len_big + (p - A.n_big) * A.len_small;
+}
+__device__ __forceinline__ int patch_len(int p, const GNArgs &A) {
+  return p < A.n_big ? A.len_big : A.len_small;
+}
+// the patch holding element column x (x < L)
+__device__ __forceinline__ int patch_of(int x, const GNArgs &A) {
+  const int nb = A.n_big * A.len_big;
+  return x < nb ? x / A.len_big : A.n_big + (x - nb) / max(A.len_small, 1);
+}
+
+template <int DT, int VB>
+__global__ __launch_bounds__(kRowsThreads) void gn_stats_rows_kernel(const GNArgs A) {
+  constexpr int V = VecInfo<DT, VB>::V;
+  constexpr int EB = Elem<DT>::bytes;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int c = b & (A.CPP - 1);
+  const int ng = b >> A.log2CPP; // n * G + g
+  const int Wv = A.L / V;        // vectors per row, 1..kRowsThreads (checked on the host)
+  const int rpi = kRowsThreads / Wv; // rows per pass of the block
+  const int lr = tid / Wv, col = tid - lr * Wv;
+  const bool active = lr < rpi;
+  const int64_t rows = (int64_t)A.Cg * A.mid; // the group is rows x L contiguous elements
+  const int64_t per = (rows + A.CPP - 1) / A.CPP;
+  const int64_t r0 = (int64_t)c * per;
+  const int64_t r1 = min(r0 + per, rows);
+  const char *gbase = (const char *)A.x + (int64_t)ng * A.Cg * A.S * EB + (int64_t)col * V * EB;
+
+  Vec<VB> v[kStatsBatch];
+  auto load_batch = [&](int64_t r) {
+#pragma unroll
+    for (int u = 0; u < kStatsBatch; ++u) {
+      const int64_t rr = r + (int64_t)u * rpi;
+      if (active && rr < r1) v[u] = vload<VB, false>(gbase + rr * A.L * EB);
+    }
+  };
+  float s1 = 0.f, s2 = 0.f, cnt = 0.f;
+  auto accumulate = [&](int64_t r, float K) {
+#pragma unroll
+    for (int u = 0; u < kStatsBatch; ++u) {
+      if (active && r + (int64_t)u * rpi < r1) {
+        float f[V];
+        unpack<DT, VB>(v[u], f);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          const float d = f[k] - K;
+          s1 += d;
+          s2 = fmaf(d, d, s2);
+        }
+        cnt += (float)V;
+      }
+    }
+  };
+  // first batch before the group shift K_g, as in gn_stats_kernel
+  const int64_t step = (int64_t)rpi * kStatsBatch;
+  int64_t r = r0 + lr;
+  load_batch(r);
+  const int64_t g0 = (int64_t)ng * A.Cg * A.S;
+  const float K = widen<DT>(load_elem<DT>(A.x, g0));
+  accumulate(r, K);
+  for (r += step; r < r1; r += step) {
+    load_batch(r);
+    accumulate(r, K);
+  }
+  Stat st{cnt, 0.f, 0.f};
+  if (cnt > 0.f) {
+    const float m = s1 / cnt;
+    st.mean = m;
+    st.m2 = fmaxf(s2 - s1 * m, 0.f);
+  }
+
+  __shared__ Stat s_st[kRowsThreads];
+  s_st[tid] = st;
+  // rows: row lr takes in row lr + h (same column) while the rows left halve
+  for (int n = rpi; n > 1;) {
+    const int h = (n + 1) >> 1;
+    __syncthreads();
+    if (active && lr < n - h) s_st[tid] = chan_merge(s_st[tid], s_st[tid + h * Wv]);
+    n = h;
+  }
+  __syncthreads();
+  // columns of row 0: within each patch, column k takes in column k + s
+  const int wmax = max(A.len_big, A.len_small) / V; // widest patch, in vectors
+  int c0 = 0, c1 = 0;
+  if (tid < Wv) {
+    const int p = patch_of(tid * V, A);
+    c0 = patch_start(p, A) / V;
+    c1 = c0 + patch_len(p, A) / V;
+  }
+  for (int s = 1; s < wmax; s <<= 1) {
+    if (tid < Wv && ((tid - c0) & (2 * s - 1)) == 0 && tid + s < c1)
+      s_st[tid] = chan_merge(s_st[tid], s_st[tid + s]);
+    __syncthreads();
+  }
+  if (tid < A.P) {
+    const Stat m = patch_len(tid, A) > 0 ? s_st[patch_start(tid, A) / V] : Stat{0.f, 0.f, 0.f};
+    float4 *dst = reinterpret_cast<float4 *>(A.part) + ((int64_t)ng * A.P + tid) * A.CPP + c;
+    *dst = make_float4(m.n, m.mean, m.m2, K);
+  }
+}
+
+
 template <int DT, int VB, bool XFIRST>
 __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   constexpr int V = VecInfo<DT, VB>::V;
@@ -271,7 +387,11 @@ static hipError_t launch_gn(const GNArgs &a, hipStream_t st) {
   const FastDiv db = make_fastdiv((uint32_t)(rb > 0 ? rb : 1));
   const FastDiv ds = make_fastdiv((uint32_t)(rs > 0 ? rs : 1));
   const unsigned blocks1 = (unsigned)((int64_t)a.N * a.G * a.P * a.CPP);
-  hipLaunchKernelGGL((gn_stats_kernel<DT, VB>), dim3(blocks1), dim3(256), 0, st, a, db, ds);
+  if (a.rows_layout)
+    hipLaunchKernelGGL((gn_stats_rows_kernel<DT, VB>), dim3((unsigned)((int64_t)a.N * a.G * a.CPP)),
+                       dim3(kRowsThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((gn_stats_kernel<DT, VB>), dim3(blocks1), dim3(256), 0, st, a, db, ds);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid2((unsigned)a.chunks2, (unsigned)((int64_t)a.N * a.C));

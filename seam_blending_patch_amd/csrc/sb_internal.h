@@ -95,6 +95,7 @@ struct GNArgs {
   int64_t per2;       // vectors per pass-2 block
   FastDiv div_C, div_Cg; // plane -> (n, c) and channel -> group
   int32_t x_first;    // pass 2 requests x before the partials (small grids)
+  int32_t rows_layout; // pass 1 reads whole rows (patches cut the innermost axis)
 };
 
 // ---------------------------------------------------------------------------

@@ -83,6 +83,9 @@ CASES = [
     ((2, 4, 100), 2, 2, 3),          # 3-D
     ((1, 64, 40, 40), 32, 2, 1),     # a single patch
     ((1, 8192, 16, 16), 64, 2, 3),   # 8192 normalise blocks: the large-grid load order
+    ((1, 8, 6, 5), 2, 3, 9),         # W split, more patches than columns: empty patches
+    ((1, 4, 3, 4096), 2, 3, 4),      # W split, rows of 512-1024 vectors
+    ((1, 4, 3, 8192), 2, 3, 3),      # W split, ragged, rows wider than one block: patch-run path
 ]
 
 
