@@ -116,8 +116,9 @@ def test_in_place_and_deterministic(sb):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-def test_misaligned_input_takes_the_scalar_path(sb):
-    gw = _gw((1, 16, 32, 32), "bf16", 4, 2, 4, seed=3)
+@pytest.mark.parametrize("axis", [2, 3])  # patches along H (runs) or W (whole rows per block)
+def test_misaligned_input_takes_the_scalar_path(sb, axis):
+    gw = _gw((1, 16, 32, 32), "bf16", 4, axis, 4, seed=3)
     x, g, b = workloads.draw_groupnorm(gw)
     xd = to_dev(x, "bf16")
     buf = torch.empty(xd.numel() + 1, dtype=xd.dtype, device=xd.device)
