@@ -154,6 +154,24 @@ def test_one_group_and_one_channel_per_group(sb, G):
     check(sb, gw, x, g, b, f"G={G}")
 
 
+def test_the_largest_plane_count(sb):
+    # N*C = 65535 planes, the normalise grid's largest y extent; one more is
+    # rejected on the host before anything is enqueued
+    gw = _gw((1, 65535, 16), "bf16", 257, 2, 2, seed=23)
+    x, g, b = workloads.draw_groupnorm(gw)
+    check(sb, gw, x, g, b, "65535 planes")
+    with pytest.raises(sb.SeamBlendError):
+        sb.patch_groupnorm(torch.zeros((1, 65536, 16), dtype=torch.bfloat16, device="cuda"), 256, 2, 2)
+
+
+def test_w_split_rows_of_1024_vectors(sb):
+    # bf16 rows of 8192 elements split into 4: one row per pass of the
+    # 1024-lane statistics block
+    gw = _gw((1, 4, 2, 8192), "bf16", 2, 3, 4, seed=24)
+    x, g, b = workloads.draw_groupnorm(gw)
+    check(sb, gw, x, g, b, "1024-vector rows")
+
+
 def test_graph_replay_with_changed_inputs(sb):
     # the two passes captured in a HIP graph: every replay, with new x between
     # replays and eager work around them, equals the eager result
