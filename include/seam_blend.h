@@ -112,8 +112,9 @@ size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape, int64_t g
 /*
  * GroupNorm of x viewed as n_patches patches along split_axis.
  *   x            device pointer, contiguous [N, C, spatial...] of dtype, ndim 3..5.
- *   shape        host array of ndim extents; C % groups == 0; N*C <= 65535
- *                (else SB_EGEOM).
+ *   shape        host array of ndim extents; C % groups == 0; N*C < 2^31 and
+ *                each group (C/G * spatial elements) < 2^31 elements (else
+ *                SB_EGEOM).
  *   split_axis   2 <= split_axis < ndim: the spatial axis the patches cut.
  *   n_patches    1..64.  Patch p covers [s_p, s_p + len_p) along split_axis
  *                with the first (L mod P) patches one longer (empty patches
@@ -132,9 +133,13 @@ size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape, int64_t g
  * positions, obtained by Chan-merging fp32 partial statistics in a fixed order
  * (chunks of a patch, then patches); var = M2 / count; rstd = 1/sqrt(var+eps);
  * y = (x - mean) * rstd * gamma_c + beta_c in fp32, rounded once to dtype.
- * Statistics are taken about a shift K_g (the group's first element), so the
- * mean is carried as K_g + m and x - mean is formed as (x - K_g) - m: inputs
- * whose mean is large against their spread keep full fp32 accuracy.
+ * Each thread folds its values into (count, mean, M2) a batch at a time: the
+ * batch's mean and squared deviations by two passes, then a Chan merge
+ * (Welford's update), so M2 is never a difference of power sums.  Statistics
+ * are taken about a shift K_g (the median of five of the group's elements,
+ * spread over it), so the mean is carried as K_g + m and x - mean is formed as
+ * (x - K_g) - m: inputs whose mean is large against their spread keep full
+ * fp32 accuracy, and up to two outlying samples never become the shift.
  * Deterministic: the same inputs give the same bits on every call.
  */
 int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t groups,

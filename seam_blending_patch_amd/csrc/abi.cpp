@@ -374,6 +374,10 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
 // --------------------------------------------------------------------------
 namespace {
 
+// largest pass-1 grid: blocks of 256 threads (1024 for the whole-row
+// layout) within 2^32 work-items in x
+constexpr int64_t kMaxStatsBlocks = ((int64_t)1 << 32) / 1024 - 1;
+
 struct GNPlan {
   sb::GNArgs a;
   bool vec16 = false;
@@ -430,8 +434,10 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
   // patches across the innermost axis: pass 1 reads whole rows of at most
   // 1024 vectors, one lane per column (see gn_stats_rows_kernel)
   a.rows_layout = (inner == 1 && a.L / V >= 1 && a.L / V <= 1024) ? 1 : 0;
-  const int64_t group_vec = (int64_t)a.Cg * S / V;
-  if (group_vec >= ((int64_t)1 << 31)) return fail(SB_EGEOM, "a group exceeds 2^31 vectors");
+  // a group's element and vector indices and its statistics counts are 32-bit
+  if ((int64_t)a.Cg * S >= ((int64_t)1 << 31)) return fail(SB_EGEOM, "a group exceeds 2^31 elements");
+  // (n, c) planes are 32-bit indices
+  if ((int64_t)a.N * a.C >= ((int64_t)1 << 31)) return fail(SB_EGEOM, "N*C must be below 2^31");
   if (S / V >= ((int64_t)1 << 40)) return fail(SB_EGEOM, "plane too large");
   // chunks per patch: a power of two, P_pow2 * CPP <= 64 (one wavefront merges
   // the partials of a group), at least 8192 elements per chunk (measured best
@@ -446,16 +452,23 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
 #ifndef SB_GN_CHUNK_MIN
 #define SB_GN_CHUNK_MIN 8192
 #endif
-  while (cpp * 2 * ppow <= 64 && patch_el / (cpp * 2) >= SB_GN_CHUNK_MIN) cpp *= 2;
+  // pass 1 launches at most kMaxStatsBlocks blocks (2^32 work-items of 256
+  // threads in x): more chunks only while the grid stays within that
+  // (counted for the per-patch layout, which has the most blocks, so that the
+  // chunk count and the workspace do not depend on the vector width)
+  const int64_t units = (int64_t)a.N * a.G * n_patches; // blocks at one chunk per patch
+  if (units > kMaxStatsBlocks)
+    return fail(SB_EGEOM, "N*groups*patches = %lld exceeds %lld statistics blocks", (long long)units,
+                (long long)kMaxStatsBlocks);
+  while (cpp * 2 * ppow <= 64 && patch_el / (cpp * 2) >= SB_GN_CHUNK_MIN && units * cpp * 2 <= kMaxStatsBlocks)
+    cpp *= 2;
   a.CPP = (int32_t)cpp;
   a.log2CPP = 0;
   while ((1 << a.log2CPP) < cpp) a.log2CPP++;
   a.per2 = 256 * sb::kNormUnroll; // vectors per pass-2 block (256 threads x kNormUnroll)
   a.chunks2 = (int32_t)std::max<int64_t>(1, (S / V + a.per2 - 1) / a.per2);
-  // pass 2 runs on a (chunks of a plane, planes) grid: at most 65535 blocks in
-  // y and 2^32 work-items in x
-  if ((int64_t)a.N * a.C > 65535) return fail(SB_EGEOM, "N*C = %lld exceeds 65535 planes",
-                                              (long long)((int64_t)a.N * a.C));
+  // pass 2 runs on a (chunks of a plane, planes) grid: 2^32 work-items in x;
+  // planes beyond the grid's y extent take further launches
   if ((int64_t)a.chunks2 * 256 >= ((int64_t)1 << 32)) return fail(SB_EGEOM, "plane too large");
   a.div_C = sb::make_fastdiv((uint32_t)std::max(a.C, 1));
   a.div_Cg = sb::make_fastdiv((uint32_t)std::max(a.Cg, 1));

@@ -393,13 +393,18 @@ __device__ __forceinline__ bool blend_item(const BlendArgs &A, float2 *s_tab, ui
     for (int x = tid; x < ews; x += nthr) s_cw[x] = coefficients(x, ew);
   if (A.E[1] > 0) {
     // the seam rows of each tile row the band meets (block-uniform loop; a
-    // band aligned to the row seams meets one tile row)
+    // band aligned to the row seams meets one tile row).  Only the seam rows
+    // inside the tile row's crop are output rows of that tile row: a seam
+    // longer than the crop (e_h > R_h on a middle tile row) runs into the
+    // next tile row's rows, whose entries that row writes, so each output row
+    // gets exactly one writer.
     const int ib2 = min((int)fdiv((uint32_t)(yo1 - 1), A.div_Rh), nh - 1);
     int hi = hia, hp = hiam;
     for (int i = ia;;) {
       const int eh = i > 0 ? min(A.E[1], min(hp, hi)) : 0;
+      const int ehs = min(eh, i < nh - 1 ? A.R[1] : hi);
       const int ybase = i * A.R[1];
-      const int lo = max(yo0, ybase), hi_row = min(yo1, ybase + eh);
+      const int lo = max(yo0, ybase), hi_row = min(yo1, ybase + ehs);
       if (hi_row > lo) {
         tables = true;
         for (int k = lo - yo0 + tid; k < hi_row - yo0; k += nthr) s_ch[k] = coefficients(yo0 + k - ybase, eh);

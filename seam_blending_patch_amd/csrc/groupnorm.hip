@@ -7,30 +7,38 @@
 // GroupNorm -- global mean, variance = M2 / count (no Bessel correction).
 // Patches follow the Patchify split (first L mod P patches one longer).
 //
-// Every statistic is kept about a group shift K_g, the group's first element
-// (any data value of the group serves; it keeps fp32 deviations small when the
-// mean is large against the spread, so the mean is carried as K_g + m with a
-// small, accurately represented m, and x - mean is formed as (x - K_g) - m).
+// Every statistic is kept about a group shift K_g, the median of five of the
+// group's elements spread over it.  Any value of the group would do as a
+// shift; one near the mean keeps the fp32 deviations x - K_g, and the mean
+// carried as K_g + m, accurate when the mean is large against the spread, and
+// taking the median of five keeps up to two outlying samples from being the
+// shift.  x - mean is then formed as (x - K_g) - m.
 //
 // Pass 1 (gn_stats_kernel): one block per (n, g, patch, chunk of the patch).
-//   Each thread accumulates the sum and sum of squares of x - K_g, turns
-//   them into (count, m, M2), and the block merges those with Chan's pairwise
-//   formula
+//   Each thread reads its vectors in batches of a few 16-byte loads.  A batch
+//   gets its own count, mean and M2 by two passes over its registers (mean of
+//   x - K_g, then the sum of squared deviations from that mean, so M2 never
+//   comes from a difference of power sums), and is merged into the thread's
+//   running (count, m, M2) with Chan's pairwise formula
 //       d = mu_B - mu_A, n = n_A + n_B, mu = mu_A + d n_B / n,
 //       M2 = M2_A + M2_B + d^2 n_A n_B / n
-//   first across the wavefront with shuffles, then across the 4 waves in LDS.
-//   One fp32 partial (count, m, M2, K_g) per block goes to the workspace.
+//   (Welford's update, a batch at a time).  The block merges its threads the
+//   same way, first across the wavefront with shuffles, then across the 4
+//   waves in LDS, and writes one partial (count, m, M2, K_g) to the workspace;
+//   counts are integers.
 // Pass 2 (gn_norm_kernel): one block per (n, c) plane chunk.  Every wave
 //   requests the P x CPP partials of its group, gamma, beta and its vectors
-//   of x, and merges the partials with a fixed shuffle tree (chunks of a patch first, then patches) -- the
-//   same order in every block, so results are deterministic -- and streams
-//   y = ((x - K_g) - m) * (rstd * gamma_c) + beta_c back out with nontemporal
-//   stores.  K_g comes from the workspace, not from x, so out may alias x.
-//   Wave 0 of the first block of each group writes the optional per-patch
-//   statistics.
+//   of x, and merges the partials with a fixed shuffle tree (chunks of a patch
+//   first, then patches) -- the same order in every block, so results are
+//   deterministic -- and streams y = ((x - K_g) - m) * (rstd * gamma_c) +
+//   beta_c back out with nontemporal stores.  K_g comes from the workspace,
+//   not from x, so out may alias x.  Wave 0 of the first block of each group
+//   writes the optional per-patch statistics.
 
 #include "sb_internal.h"
 #include "sb_vec.h"
+
+#include <algorithm>
 
 #ifndef SB_GN_NT_STORE
 #define SB_GN_NT_STORE 1 // nontemporal hints on y stores (measured faster here, unlike the blend)
@@ -41,26 +49,30 @@
 
 namespace sb {
 
+// Statistics of a set of values: integer count, mean and sum of squared
+// deviations from the mean (both about the group shift).
 struct Stat {
-  float n, mean, m2;
+  uint32_t n;
+  float mean, m2;
 };
 
+// Chan, Golub & LeVeque's pairwise merge; an empty side is the identity.
 __device__ __forceinline__ Stat chan_merge(const Stat &a, const Stat &b) {
-  if (b.n == 0.f) return a;
-  if (a.n == 0.f) return b;
-  const float n = a.n + b.n;
+  if (b.n == 0) return a;
+  if (a.n == 0) return b;
+  const uint32_t n = a.n + b.n;
   const float d = b.mean - a.mean;
-  const float r = b.n / n;
+  const float r = (float)b.n / (float)n;
   Stat o;
   o.n = n;
   o.mean = a.mean + d * r;
-  o.m2 = a.m2 + b.m2 + d * d * a.n * r;
+  o.m2 = a.m2 + b.m2 + d * d * (float)a.n * r;
   return o;
 }
 
 __device__ __forceinline__ Stat shfl_down_stat(const Stat &s, int o) {
   Stat t;
-  t.n = __shfl_down(s.n, o, 64);
+  t.n = (uint32_t)__shfl_down((int)s.n, o, 64);
   t.mean = __shfl_down(s.mean, o, 64);
   t.m2 = __shfl_down(s.m2, o, 64);
   return t;
@@ -70,6 +82,67 @@ __device__ __forceinline__ Stat shfl_down_stat(const Stat &s, int o) {
 #define SB_GN_STATS_BATCH 4
 #endif
 constexpr int kStatsBatch = SB_GN_STATS_BATCH; // vectors per thread whose loads are in flight together
+
+template <int DT> __device__ __forceinline__ uint32_t load_elem(const void *p, int64_t i) {
+  return DT == DT_F32 ? ((const uint32_t *)p)[i] : (uint32_t)((const uint16_t *)p)[i];
+}
+
+// The group shift: the median of five of the group's elements, at offsets
+// 0, len/4, len/2, 3len/4 and len-1 of its Cg * S contiguous elements from
+// g0, so that up to two outlying samples never become the shift.  The median
+// is element 2 of a 9-comparator sorting network on the five.
+template <int DT>
+__device__ __forceinline__ float group_shift(const void *x, int64_t g0, int64_t len) {
+  float v[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) v[k] = widen<DT>(load_elem<DT>(x, g0 + (k < 4 ? k * (len / 4) : len - 1)));
+  constexpr int net[9][2] = {{0, 1}, {3, 4}, {2, 4}, {2, 3}, {0, 3}, {0, 2}, {1, 4}, {1, 3}, {1, 2}};
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const float lo = fminf(v[net[k][0]], v[net[k][1]]), hi = fmaxf(v[net[k][0]], v[net[k][1]]);
+    v[net[k][0]] = lo;
+    v[net[k][1]] = hi;
+  }
+  return v[2];
+}
+
+// Merges one batch of up to kStatsBatch vectors (those with ok[u] set) into
+// the running statistics st: the batch's own mean and M2 by two passes over
+// the registers, then one Chan merge.
+template <int DT, int VB>
+__device__ __forceinline__ void accumulate_batch(Stat &st, const Vec<VB> (&v)[kStatsBatch],
+                                                 const bool (&ok)[kStatsBatch], float K) {
+  constexpr int V = VecInfo<DT, VB>::V;
+  float d[kStatsBatch][V];
+  float s = 0.f;
+  uint32_t nb = 0;
+#pragma unroll
+  for (int u = 0; u < kStatsBatch; ++u) {
+    if (ok[u]) {
+      unpack<DT, VB>(v[u], d[u]);
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        d[u][k] -= K;
+        s += d[u][k];
+      }
+      nb += V;
+    }
+  }
+  if (nb == 0) return;
+  const float mb = nb == (uint32_t)(kStatsBatch * V) ? s * (1.0f / (float)(kStatsBatch * V))
+                                                      : s / (float)nb;
+  float q = 0.f;
+#pragma unroll
+  for (int u = 0; u < kStatsBatch; ++u)
+    if (ok[u]) {
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const float t = d[u][k] - mb;
+        q = fmaf(t, t, q);
+      }
+    }
+  st = chan_merge(st, Stat{nb, mb, q});
+}
 
 template <int DT, int VB>
 __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv div_big,
@@ -95,62 +168,36 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
   const uint32_t q0 = (uint32_t)c * per;
   const uint32_t q1 = min(q0 + per, totalv);
   const int64_t row = (int64_t)A.L * A.inner; // elements between consecutive runs
-  const char *gbase = (const char *)A.x +
-                      (((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S + (int64_t)start * A.inner) * EB;
+  const int64_t g0 = ((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S;
+  const char *gbase = (const char *)A.x + (g0 + (int64_t)start * A.inner) * EB;
 
   // Vectors q0 + tid + k * blockDim.x, in batches of kStatsBatch whose loads
   // are issued together.
   Vec<VB> v[kStatsBatch];
+  bool ok[kStatsBatch];
   auto load_batch = [&](uint32_t base) {
 #pragma unroll
     for (int u = 0; u < kStatsBatch; ++u) {
       const uint32_t q = base + u * blockDim.x;
-      if (q < q1) {
+      ok[u] = q < q1;
+      if (ok[u]) {
         const uint32_t r = fdiv(q, dv);
         const uint32_t pos = q - r * runv;
         v[u] = vload<VB, false>(gbase + ((int64_t)r * row + (int64_t)pos * V) * EB);
       }
     }
   };
-  float s1 = 0.f, s2 = 0.f, cnt = 0.f;
-  auto accumulate = [&](uint32_t base, float K) {
-#pragma unroll
-    for (int u = 0; u < kStatsBatch; ++u) {
-      if (base + u * blockDim.x < q1) {
-        float f[V];
-        unpack<DT, VB>(v[u], f);
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-          const float d = f[k] - K;
-          s1 += d;
-          s2 = fmaf(d, d, s2);
-        }
-        cnt += (float)V;
-      }
-    }
-  };
-  // The first batch is issued before the group shift K_g (the group's first
-  // element) is read, so the two share one memory latency; every later batch
-  // finds K_g in a register.
+  // The first batch is issued before the group shift is read, so the two
+  // share one memory latency; every later batch finds K_g in a register.
+  Stat st{0u, 0.f, 0.f};
   const uint32_t step = blockDim.x * kStatsBatch;
   uint32_t base = q0 + tid;
   load_batch(base);
-  const int64_t g0 = ((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S;
-  const float K = widen<DT>(DT == DT_F32 ? ((const uint32_t *)A.x)[g0] : ((const uint16_t *)A.x)[g0]);
-  accumulate(base, K);
+  const float K = group_shift<DT>(A.x, g0, (int64_t)A.Cg * A.S);
+  accumulate_batch<DT, VB>(st, v, ok, K);
   for (base += step; base < q1; base += step) {
     load_batch(base);
-    accumulate(base, K);
-  }
-  Stat st;
-  st.n = cnt;
-  if (cnt > 0.f) {
-    const float m = s1 / cnt; // mean of x - K_g
-    st.mean = m;
-    st.m2 = fmaxf(s2 - s1 * m, 0.f);
-  } else {
-    st.mean = 0.f;
-    st.m2 = 0.f;
+    accumulate_batch<DT, VB>(st, v, ok, K);
   }
   // wavefront tree, lane l merges lane l + o
   const int lane = tid & 63;
@@ -166,12 +213,8 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
     Stat m = s_w[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = chan_merge(m, s_w[w]);
     float4 *dst = reinterpret_cast<float4 *>(A.part) + b;
-    *dst = make_float4(m.n, m.mean, m.m2, K);
+    *dst = make_float4(__uint_as_float(m.n), m.mean, m.m2, K);
   }
-}
-
-template <int DT> __device__ __forceinline__ uint32_t load_elem(const void *p, int64_t i) {
-  return DT == DT_F32 ? ((const uint32_t *)p)[i] : (uint32_t)((const uint16_t *)p)[i];
 }
 
 // Pass 1 when the patches cut the innermost axis (a W split): a patch run is
@@ -214,49 +257,29 @@ __global__ __launch_bounds__(kRowsThreads) void gn_stats_rows_kernel(const GNArg
   const int64_t per = (rows + A.CPP - 1) / A.CPP;
   const int64_t r0 = (int64_t)c * per;
   const int64_t r1 = min(r0 + per, rows);
-  const char *gbase = (const char *)A.x + (int64_t)ng * A.Cg * A.S * EB + (int64_t)col * V * EB;
+  const int64_t g0 = (int64_t)ng * A.Cg * A.S;
+  const char *gbase = (const char *)A.x + g0 * EB + (int64_t)col * V * EB;
 
   Vec<VB> v[kStatsBatch];
+  bool ok[kStatsBatch];
   auto load_batch = [&](int64_t r) {
 #pragma unroll
     for (int u = 0; u < kStatsBatch; ++u) {
       const int64_t rr = r + (int64_t)u * rpi;
-      if (active && rr < r1) v[u] = vload<VB, false>(gbase + rr * A.L * EB);
+      ok[u] = active && rr < r1;
+      if (ok[u]) v[u] = vload<VB, false>(gbase + rr * A.L * EB);
     }
   };
-  float s1 = 0.f, s2 = 0.f, cnt = 0.f;
-  auto accumulate = [&](int64_t r, float K) {
-#pragma unroll
-    for (int u = 0; u < kStatsBatch; ++u) {
-      if (active && r + (int64_t)u * rpi < r1) {
-        float f[V];
-        unpack<DT, VB>(v[u], f);
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-          const float d = f[k] - K;
-          s1 += d;
-          s2 = fmaf(d, d, s2);
-        }
-        cnt += (float)V;
-      }
-    }
-  };
-  // first batch before the group shift K_g, as in gn_stats_kernel
+  // first batch before the group shift, as in gn_stats_kernel
+  Stat st{0u, 0.f, 0.f};
   const int64_t step = (int64_t)rpi * kStatsBatch;
   int64_t r = r0 + lr;
   load_batch(r);
-  const int64_t g0 = (int64_t)ng * A.Cg * A.S;
-  const float K = widen<DT>(load_elem<DT>(A.x, g0));
-  accumulate(r, K);
+  const float K = group_shift<DT>(A.x, g0, (int64_t)A.Cg * A.S);
+  accumulate_batch<DT, VB>(st, v, ok, K);
   for (r += step; r < r1; r += step) {
     load_batch(r);
-    accumulate(r, K);
-  }
-  Stat st{cnt, 0.f, 0.f};
-  if (cnt > 0.f) {
-    const float m = s1 / cnt;
-    st.mean = m;
-    st.m2 = fmaxf(s2 - s1 * m, 0.f);
+    accumulate_batch<DT, VB>(st, v, ok, K);
   }
 
   __shared__ Stat s_st[kRowsThreads];
@@ -283,9 +306,9 @@ __global__ __launch_bounds__(kRowsThreads) void gn_stats_rows_kernel(const GNArg
     __syncthreads();
   }
   if (tid < A.P) {
-    const Stat m = patch_len(tid, A) > 0 ? s_st[patch_start(tid, A) / V] : Stat{0.f, 0.f, 0.f};
+    const Stat m = patch_len(tid, A) > 0 ? s_st[patch_start(tid, A) / V] : Stat{0u, 0.f, 0.f};
     float4 *dst = reinterpret_cast<float4 *>(A.part) + ((int64_t)ng * A.P + tid) * A.CPP + c;
-    *dst = make_float4(m.n, m.mean, m.m2, K);
+    *dst = make_float4(__uint_as_float(m.n), m.mean, m.m2, K);
   }
 }
 
@@ -296,10 +319,11 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   constexpr int EB = Elem<DT>::bytes;
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
-  const uint32_t plane = blockIdx.y; // < 2^16
+  const uint32_t plane = A.plane0 + blockIdx.y; // < 2^31 (checked on the host)
   const int n = (int)fdiv(plane, A.div_C);
   const int ch = (int)(plane - (uint32_t)n * (uint32_t)A.C);
   const int g = (int)fdiv((uint32_t)ch, A.div_Cg);
+  const int64_t ng = (int64_t)n * A.G + g;
   const int64_t Sv = A.S / V;
   const int64_t q0 = (int64_t)chunk * A.per2;
   const int64_t q1 = min(q0 + A.per2, Sv);
@@ -320,7 +344,7 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   uint32_t graw, braw;
   Vec<VB> xs[kNormUnroll];
   auto load_small = [&]() {
-    if (lane < K) src = reinterpret_cast<const float4 *>(A.part)[(int64_t)(n * A.G + g) * K + lane];
+    if (lane < K) src = reinterpret_cast<const float4 *>(A.part)[ng * K + lane];
     graw = load_elem<DT>(A.gamma ? A.gamma : A.x, A.gamma ? ch : 0);
     braw = load_elem<DT>(A.beta ? A.beta : A.x, A.beta ? ch : 0);
   };
@@ -342,24 +366,24 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   const float bet = A.beta ? widen<DT>(braw) : 0.0f;
 
   // merge the group's partials
-  Stat st{src.x, src.y, src.z};
+  Stat st{__float_as_uint(src.x), src.y, src.z};
   const float kg = src.w; // the group shift K_g (the same in every partial of the group)
   const float Kg = __shfl(kg, 0, 64);
   const bool writer = A.patch_stats != nullptr && chunk == 0 && ch == g * A.Cg && tid < 64;
   if (writer && A.CPP == 1 && lane < A.P) {
-    float *d = A.patch_stats + ((int64_t)(n * A.G + g) * A.P + lane) * 3;
-    d[0] = st.n; d[1] = st.n > 0.f ? Kg + st.mean : 0.f; d[2] = st.m2;
+    float *d = A.patch_stats + (ng * A.P + lane) * 3;
+    d[0] = (float)st.n; d[1] = st.n > 0 ? Kg + st.mean : 0.f; d[2] = st.m2;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const Stat t = shfl_down_stat(st, o);
     if ((lane & (2 * o - 1)) == 0 && lane + o < 64) st = chan_merge(st, t);
     if (writer && 2 * o == A.CPP && (lane & (A.CPP - 1)) == 0 && (lane >> A.log2CPP) < A.P) {
-      float *d = A.patch_stats + ((int64_t)(n * A.G + g) * A.P + (lane >> A.log2CPP)) * 3;
-      d[0] = st.n; d[1] = st.n > 0.f ? Kg + st.mean : 0.f; d[2] = st.m2;
+      float *d = A.patch_stats + (ng * A.P + (lane >> A.log2CPP)) * 3;
+      d[0] = (float)st.n; d[1] = st.n > 0 ? Kg + st.mean : 0.f; d[2] = st.m2;
     }
   }
-  const float cnt = __shfl(st.n, 0, 64);
+  const float cnt = (float)(uint32_t)__shfl((int)st.n, 0, 64);
   const float mean = __shfl(st.mean, 0, 64);
   const float m2 = __shfl(st.m2, 0, 64);
   const float var = m2 / cnt;
@@ -386,6 +410,8 @@ static hipError_t launch_gn(const GNArgs &a, hipStream_t st) {
   const int64_t rs = ((int64_t)a.len_small * a.inner) / V;
   const FastDiv db = make_fastdiv((uint32_t)(rb > 0 ? rb : 1));
   const FastDiv ds = make_fastdiv((uint32_t)(rs > 0 ? rs : 1));
+  // pass 1: one block per (n, g, patch, chunk), or per (n, g, chunk of rows);
+  // the host keeps the count below 2^24 (2^32 work-items)
   const unsigned blocks1 = (unsigned)((int64_t)a.N * a.G * a.P * a.CPP);
   if (a.rows_layout)
     hipLaunchKernelGGL((gn_stats_rows_kernel<DT, VB>), dim3((unsigned)((int64_t)a.N * a.G * a.CPP)),
@@ -394,12 +420,21 @@ static hipError_t launch_gn(const GNArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((gn_stats_kernel<DT, VB>), dim3(blocks1), dim3(256), 0, st, a, db, ds);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid2((unsigned)a.chunks2, (unsigned)((int64_t)a.N * a.C));
-  if (a.x_first)
-    hipLaunchKernelGGL((gn_norm_kernel<DT, VB, true>), grid2, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((gn_norm_kernel<DT, VB, false>), grid2, dim3(256), 0, st, a);
-  return hipGetLastError();
+  // pass 2: (chunks of a plane, planes) with at most kMaxGridY planes per
+  // launch; more planes take further launches on the same stream
+  const int64_t planes = (int64_t)a.N * a.C;
+  GNArgs w = a;
+  for (int64_t p0 = 0; p0 < planes; p0 += kMaxGridY) {
+    w.plane0 = (uint32_t)p0;
+    const dim3 grid2((unsigned)a.chunks2, (unsigned)std::min<int64_t>(kMaxGridY, planes - p0));
+    if (a.x_first)
+      hipLaunchKernelGGL((gn_norm_kernel<DT, VB, true>), grid2, dim3(256), 0, st, w);
+    else
+      hipLaunchKernelGGL((gn_norm_kernel<DT, VB, false>), grid2, dim3(256), 0, st, w);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 } // namespace sb

@@ -80,7 +80,7 @@ struct GNArgs {
   void *out;
   const void *gamma;
   const void *beta;
-  float *part;        // partials [N][G][P][CPP][4]: count, mean of x - K_g, M2, K_g
+  float *part;        // partials [N][G][P][CPP][4]: count (uint32 bits), mean of x - K_g, M2, K_g
   float *patch_stats; // optional [N][G][P][3]
   int32_t N, C, G, Cg;
   int64_t S;          // spatial elements per channel
@@ -96,7 +96,10 @@ struct GNArgs {
   FastDiv div_C, div_Cg; // plane -> (n, c) and channel -> group
   int32_t x_first;    // pass 2 requests x before the partials (small grids)
   int32_t rows_layout; // pass 1 reads whole rows (patches cut the innermost axis)
+  uint32_t plane0;    // first (n, c) plane of this pass-2 launch
 };
+
+constexpr int64_t kMaxGridY = 65535; // largest grid extent in y (pass-2 planes per launch)
 
 // ---------------------------------------------------------------------------
 // normalised-ramp blend launch arguments

@@ -101,9 +101,15 @@ def test_groupnorm_workspace_and_validation(sb):
                               ((1, 32, 8, 8), 4, 2, 0),   # no patches
                               ((1, 32, 8, 8), 4, 2, 65),  # too many patches
                               ((1, 32), 4, 2, 1),         # rank
-                              ((2, 40000, 4, 8), 8, 2, 1)]:  # N*C above 65535 planes
+                              ((1, 2, 1 << 15, 1 << 15), 1, 2, 1),  # a group of 2^31 elements
+                              ((1 << 20, 4096, 1, 1), 4096, 2, 1)]:  # N*C of 2^32 planes
         with pytest.raises(sb.SeamBlendError):
             sb.patch_groupnorm_workspace_bytes(shape, G, axis, P)
+    # more (n, c) planes than one launch's grid holds in y: accepted (pass 2
+    # takes several launches); one chunk per patch at 8 elements per chunk
+    assert sb.patch_groupnorm_workspace_bytes((2, 65536, 4, 4), 256, 2, 2) == 2 * 256 * 2 * 16
+    # a group just below 2^31 elements is accepted
+    assert sb.patch_groupnorm_workspace_bytes((1, 2, (1 << 15) - 1, 1 << 15), 1, 2, 1) > 0
 
 
 def test_groupnorm_rejects_small_workspace_and_bad_args_on_host(sb):

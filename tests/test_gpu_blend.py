@@ -102,6 +102,23 @@ def test_edge_cases(sb, dtype):
         check(sb, w, workloads.draw_tiles(w), "edge")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_row_seam_longer_than_the_crop_in_tall_bands(sb, dtype):
+    # A middle tile row whose clamped seam (199 rows) is longer than its crop
+    # (the 64-row limit), then a short last row, in one narrow tile column:
+    # the row bands are about 84 rows tall and not aligned to the tile rows,
+    # so one band meets both rows' seams and its row-coefficient table holds
+    # entries of two tile rows (across more than one wavefront).
+    narrow = 32 if dtype == "fp32" else 64  # 8 vectors per row
+    cases = [
+        _wl(dtype, [300, 300, 40], [narrow], 199, 64, C=2),
+        _wl(dtype, [400, 400, 400, 40], [narrow], 199, 64, N=2, C=1),
+        _wl(dtype, [300, 300, 40], [narrow], 199, 64, ndim=5, ext_t=(5, 5, 2), Et=2, Rt=3, C=1),
+    ]
+    for w in cases:
+        check(sb, w, workloads.draw_tiles(w), "long seam")
+
+
 def test_many_tiles_use_several_launch_windows(sb):
     # 13 x 13 = 169 tiles exceed one launch window's pointer table
     w = _wl("fp16", [24] * 12 + [13], [24] * 12 + [16], 8, 16, C=2)

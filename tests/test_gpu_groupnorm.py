@@ -154,14 +154,40 @@ def test_one_group_and_one_channel_per_group(sb, G):
     check(sb, gw, x, g, b, f"G={G}")
 
 
-def test_the_largest_plane_count(sb):
-    # N*C = 65535 planes, the normalise grid's largest y extent; one more is
-    # rejected on the host before anything is enqueued
-    gw = _gw((1, 65535, 16), "bf16", 257, 2, 2, seed=23)
+def test_more_planes_than_one_launch_holds(sb):
+    # N*C = 131072 (n, c) planes: the normalise pass takes its planes in
+    # launches of at most 65535 (the grid's y extent)
+    gw = _gw((2, 65536, 4, 4), "bf16", 256, 2, 2, seed=23)
     x, g, b = workloads.draw_groupnorm(gw)
-    check(sb, gw, x, g, b, "65535 planes")
-    with pytest.raises(sb.SeamBlendError):
-        sb.patch_groupnorm(torch.zeros((1, 65536, 16), dtype=torch.bfloat16, device="cuda"), 256, 2, 2)
+    check(sb, gw, x, g, b, "131072 planes")
+
+
+@pytest.mark.parametrize("shape,G,axis,P", [
+    ((1, 512, 256, 256), 32, 2, 4),   # decoder activation, patches along H
+    ((2, 256, 512, 512), 32, 3, 8),   # decoder activation, patches along W (whole-row pass 1)
+    ((1, 64, 640, 1024), 2, 2, 3),    # groups of 20,971,520 elements (more than 2^24)
+])
+def test_fp32_decoder_size_groups(sb, shape, G, axis, P):
+    # fp32 at the 1e-5 reading with groups of 10^6 to 2 x 10^7 elements: long
+    # per-thread runs and deep merges
+    gw = _gw(shape, "fp32", G, axis, P, seed=31)
+    x, g, b = workloads.draw_groupnorm(gw)
+    check(sb, gw, x, g, b, "fp32 decoder size")
+
+
+@pytest.mark.parametrize("where", ["first", "first-and-middle"])
+@pytest.mark.parametrize("value", [100.0, 1000.0])
+def test_fp32_outlying_samples(sb, where, value):
+    # N(0,1) groups with an outlier at the group's first element (and its
+    # middle one): the statistics must not lose the variance to cancellation
+    # against an outlying shift, at the fp32 1e-5 reading
+    gw = _gw((1, 32, 32, 256), "fp32", 4, 2, 2, seed=32, offset=None)
+    x, g, b = workloads.draw_groupnorm(gw)
+    per = x.reshape(gw.shape[0], gw.groups, -1)
+    per[:, :, 0] = value
+    if where == "first-and-middle":
+        per[:, :, per.shape[2] // 2] = value
+    check(sb, gw, x, g, b, f"outlier {value} at {where}")
 
 
 def test_w_split_rows_of_1024_vectors(sb):
