@@ -148,6 +148,27 @@ int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t group
                     size_t workspace_bytes, float *patch_stats, void *stream);
 
 /*
+ * patch_groupnorm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results, with the statistics partials in
+ * a static scratch array the library holds on each GPU instead of a
+ * caller-given workspace.  The caller still passes x, out (and gamma, beta,
+ * patch_stats).  Allocates nothing and calls no allocating routine; its first
+ * call on a device looks the array's device address up once.
+ *   Limit: problems whose partials exceed SB_GN_STATIC_SCRATCH_BYTES
+ *   (patch_groupnorm_workspace_bytes() > 1 MiB, i.e. N*groups*patches*chunks
+ *   above 65536) return SB_EWORKSPACE before anything is enqueued.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (for example on two streams) race and must be ordered by the caller.
+ * Arguments, layout and errors otherwise as patch_groupnorm.
+ */
+#define SB_GN_STATIC_SCRATCH_BYTES (1u << 20)
+int patch_groupnorm_noalloc(const void *x, int ndim, const int64_t *shape, int64_t groups,
+                            int split_axis, int64_t n_patches, float eps, const void *gamma,
+                            const void *beta, int dtype, void *out, float *patch_stats,
+                            void *stream);
+
+/*
  * Normalised-ramp blend of wide tiles (unsloth Studio PR "size seam-free VAE
  * tiles from measured peaks", the Qwen-Image-2.1 wide-tile commit, which
  * the later commits extend to every image VAE and to the tiled encode).

@@ -18,6 +18,7 @@ import torch
 
 __all__ = ["vae_tile_layout", "LAYOUT_RULES", "vae_tile_ramp_blend", "RampBlend", "vae_tile_blend_stitch", "vae_tile_blend_stitch_output_extents", "BlendStitch",
            "patch_groupnorm", "patch_groupnorm_workspace_bytes", "PatchGroupNorm",
+           "patch_groupnorm_noalloc", "GN_STATIC_SCRATCH_BYTES",
            "SeamBlendError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseamblend.so")
@@ -39,6 +40,10 @@ _lib.patch_groupnorm.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64p, ctypes.c_
                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p, ctypes.c_void_p]
 _lib.patch_groupnorm.restype = ctypes.c_int
+_lib.patch_groupnorm_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64p, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.patch_groupnorm_noalloc.restype = ctypes.c_int
 _lib.vae_tile_layout.argtypes = [ctypes.c_int64, ctypes.c_int, _i64p, ctypes.c_int64, _i64p, _i64p, _i64p]
 _lib.vae_tile_layout.restype = ctypes.c_int
 _lib.vae_tile_ramp_blend.argtypes = [ctypes.POINTER(ctypes.c_void_p), _i64p, _i64p, _i64p, _i64p, _i64p,
@@ -352,3 +357,42 @@ def patch_groupnorm(x: torch.Tensor, groups: int, split_axis: int, n_patches: in
                           patch_stats)
     with torch.cuda.device(plan.device):
         return plan()
+
+
+GN_STATIC_SCRATCH_BYTES = 1 << 20  # SB_GN_STATIC_SCRATCH_BYTES
+
+
+def patch_groupnorm_noalloc(x: torch.Tensor, groups: int, split_axis: int, n_patches: int,
+                            eps: float = 1e-6, gamma: Optional[torch.Tensor] = None,
+                            beta: Optional[torch.Tensor] = None, out: torch.Tensor = None,
+                            patch_stats: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """patch_groupnorm without a workspace: the library keeps the statistics
+    in its static per-GPU scratch (problems whose statistics need more than
+    GN_STATIC_SCRATCH_BYTES are refused).  ``out`` is required, so that the
+    call allocates nothing; calls that overlap on one GPU race."""
+    _require_gpu(x, "x")
+    if out is None:
+        raise ValueError("out is required (the call allocates nothing)")
+    _require_gpu(out, "out")
+    if tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype or out.device != x.device:
+        raise ValueError("out must match x")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _require_gpu(t, name)
+            if t.dtype != x.dtype or t.numel() != x.shape[1] or t.device != x.device:
+                raise ValueError(f"{name} must be [C] of x's dtype on x's device")
+    if patch_stats is not None and (patch_stats.dtype != torch.float32 or not patch_stats.is_cuda
+                                    or not patch_stats.is_contiguous()
+                                    or patch_stats.numel() != x.shape[0] * groups * n_patches * 3):
+        raise ValueError("patch_stats must be a contiguous float32 GPU tensor [N, G, P, 3]")
+    with torch.cuda.device(x.device):
+        rc = _lib.patch_groupnorm_noalloc(
+            ctypes.c_void_p(x.data_ptr()), x.dim(), _arr(x.shape), groups, split_axis, n_patches, float(eps),
+            ctypes.c_void_p(gamma.data_ptr() if gamma is not None else None),
+            ctypes.c_void_p(beta.data_ptr() if beta is not None else None), _DTYPE[x.dtype],
+            ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(patch_stats.data_ptr() if patch_stats is not None else None),
+            ctypes.c_void_p(_stream_ptr(x.device)))
+    if rc != 0:
+        raise SeamBlendError(rc, "patch_groupnorm_noalloc")
+    return out

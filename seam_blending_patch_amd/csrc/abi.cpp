@@ -486,10 +486,15 @@ extern "C" size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape
   return P.ws_bytes;
 }
 
-extern "C" int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t groups,
-                               int split_axis, int64_t n_patches, float eps, const void *gamma,
-                               const void *beta, int dtype, void *out, void *workspace,
-                               size_t workspace_bytes, float *patch_stats, void *stream) {
+namespace {
+
+// patch_groupnorm with its statistics partials either in the caller's
+// workspace or (workspace == nullptr and use_static) in the library's static
+// device scratch, looked up only after every host check has passed.
+int groupnorm_call(const void *x, int ndim, const int64_t *shape, int64_t groups, int split_axis,
+                   int64_t n_patches, float eps, const void *gamma, const void *beta, int dtype, void *out,
+                   void *workspace, size_t workspace_bytes, bool use_static, float *patch_stats,
+                   void *stream) {
   if (dtype != SB_F32 && dtype != SB_F16 && dtype != SB_BF16)
     return fail(SB_EARG, "unknown dtype %d", dtype);
   GNPlan P;
@@ -498,11 +503,19 @@ extern "C" int patch_groupnorm(const void *x, int ndim, const int64_t *shape, in
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(SB_EARG, "eps must be finite and >= 0");
   if (!x || !out) return fail(SB_EARG, "null x or out");
   if (P.empty) return SB_OK;
-  if (!workspace) return fail(SB_EARG, "null workspace");
-  if (workspace_bytes < P.ws_bytes)
-    return fail(SB_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
-                P.ws_bytes);
-  if (!aligned(workspace, 16) || (patch_stats && !aligned(patch_stats, 4)))
+  if (use_static) {
+    if (P.ws_bytes > (size_t)SB_GN_STATIC_SCRATCH_BYTES)
+      return fail(SB_EWORKSPACE,
+                  "the statistics of this problem need %zu bytes, more than the %zu-byte static "
+                  "scratch: call patch_groupnorm with a workspace",
+                  P.ws_bytes, (size_t)SB_GN_STATIC_SCRATCH_BYTES);
+  } else {
+    if (!workspace) return fail(SB_EARG, "null workspace");
+    if (workspace_bytes < P.ws_bytes)
+      return fail(SB_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                  P.ws_bytes);
+  }
+  if ((!use_static && !aligned(workspace, 16)) || (patch_stats && !aligned(patch_stats, 4)))
     return fail(SB_EARG, "workspace must be 16-byte and patch_stats 4-byte aligned");
   const int EB = elem_bytes(dtype);
   if (!aligned(x, EB) || !aligned(out, EB) || (gamma && !aligned(gamma, EB)) || (beta && !aligned(beta, EB)))
@@ -517,6 +530,11 @@ extern "C" int patch_groupnorm(const void *x, int ndim, const int64_t *shape, in
     // misaligned bases: the same layout with single-element vectors
     rc = plan_groupnorm(ndim, shape, groups, split_axis, n_patches, EB, false, P);
     if (rc) return rc;
+  }
+  if (use_static) {
+    hipError_t e = sb_groupnorm_static_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(SB_ELAUNCH, "static scratch lookup failed: %s", hipGetErrorString(e));
   }
   sb::GNArgs &a = P.a;
   a.x = x;
@@ -533,4 +551,22 @@ extern "C" int patch_groupnorm(const void *x, int ndim, const int64_t *shape, in
   hipError_t e = sb_launch_groupnorm(a, dtype, vec16 ? 1 : 0, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SB_ELAUNCH, "groupnorm launch failed: %s", hipGetErrorString(e));
   return SB_OK;
+}
+
+} // namespace
+
+extern "C" int patch_groupnorm(const void *x, int ndim, const int64_t *shape, int64_t groups,
+                               int split_axis, int64_t n_patches, float eps, const void *gamma,
+                               const void *beta, int dtype, void *out, void *workspace,
+                               size_t workspace_bytes, float *patch_stats, void *stream) {
+  return groupnorm_call(x, ndim, shape, groups, split_axis, n_patches, eps, gamma, beta, dtype, out,
+                        workspace, workspace_bytes, false, patch_stats, stream);
+}
+
+extern "C" int patch_groupnorm_noalloc(const void *x, int ndim, const int64_t *shape, int64_t groups,
+                                       int split_axis, int64_t n_patches, float eps, const void *gamma,
+                                       const void *beta, int dtype, void *out, float *patch_stats,
+                                       void *stream) {
+  return groupnorm_call(x, ndim, shape, groups, split_axis, n_patches, eps, gamma, beta, dtype, out,
+                        nullptr, 0, true, patch_stats, stream);
 }

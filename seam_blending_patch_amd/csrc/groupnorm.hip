@@ -38,7 +38,10 @@
 #include "sb_internal.h"
 #include "sb_vec.h"
 
+#include "../../include/seam_blend.h"
+
 #include <algorithm>
+#include <mutex>
 
 #ifndef SB_GN_NT_STORE
 #define SB_GN_NT_STORE 1 // nontemporal hints on y stores (measured faster here, unlike the blend)
@@ -444,4 +447,35 @@ hipError_t sb_launch_groupnorm(const sb::GNArgs &a, int dtype, int vec16, hipStr
   if (dtype == DT_F32) return vec16 ? launch_gn<DT_F32, 16>(a, st) : launch_gn<DT_F32, 4>(a, st);
   if (dtype == DT_F16) return vec16 ? launch_gn<DT_F16, 16>(a, st) : launch_gn<DT_F16, 2>(a, st);
   return vec16 ? launch_gn<DT_BF16, 16>(a, st) : launch_gn<DT_BF16, 2>(a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Static statistics scratch for patch_groupnorm_noalloc, for callers that
+// cannot allocate device memory.  Every GPU the library runs on holds its own
+// copy of the array until the process ends; its host-side name is not a
+// device address, so the host uses only the address hipGetSymbolAddress
+// returns for the current device, looked up once per device and kept.  The
+// partials need no clearing: pass 1 writes every entry pass 2 reads.  Every
+// call on one GPU shares that GPU's array, so calls that overlap on one GPU
+// (on different streams) race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float4 scratch[SB_GN_STATIC_SCRATCH_BYTES / sizeof(float4)];
+
+hipError_t sb_groupnorm_static_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }

@@ -149,5 +149,8 @@ hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 gr
 hipError_t sb_launch_blend_span(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                                 hipStream_t st);
 hipError_t sb_launch_groupnorm(const sb::GNArgs &a, int dtype, int vec16, hipStream_t st);
+// the current device's address of the static GroupNorm statistics scratch
+// (SB_GN_STATIC_SCRATCH_BYTES), looked up once per device
+hipError_t sb_groupnorm_static_scratch(void **ptr);
 hipError_t sb_launch_ramp(const sb::RampArgs &a, int dtype, int vec16, dim3 grid, size_t lds,
                           hipStream_t st);
