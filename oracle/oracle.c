@@ -141,7 +141,10 @@ static void store_T(void *p, int64_t idx, float v, int dtype)
     else ((float *)p)[idx] = v;
 }
 
-/* [P1] "Share coefficient construction": float64 division, one rounding to fp32 */
+/* Crossfade weights per the diffusers issue "[Proposal] Vectorize tiled VAE
+ * blending while preserving rounding and CUDA graph replay", section "Proposed
+ * scope": the ratio k/e is formed by a float64 division and each weight is
+ * rounded once to fp32 (w_a from 1 - k/e in double, never 1 - w_b in fp32). */
 void oracle_blend_coefficients(int64_t e, float *wa, float *wb)
 {
     for (int64_t k = 0; k < e; ++k) {
@@ -151,7 +154,9 @@ void oracle_blend_coefficients(int64_t e, float *wa, float *wb)
     }
 }
 
-/* one crossfaded element, [P1] "per-product rounding" */
+/* One crossfaded element (same page and section): each weighted operand is
+ * rounded to the storage type on its own before the two are added, and the
+ * sum is rounded to the storage type again. */
 float oracle_crossfade(float a, float b, float wa, float wb, int dtype)
 {
     float pa = round_T(a * wa, dtype);

@@ -352,8 +352,12 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
       A.Y0 = (int32_t)Y0; A.nY = (int32_t)(Y1 - Y0);
       A.div_nF = sb::make_fastdiv((uint32_t)A.nF);
       const int64_t row_blocks = (A.nY + rows_pb - 1) / rows_pb;
-      // grid x = (plane, frame) pairs of this window, y = W segments (or spans), z = row bands
-      const int64_t max_planes = std::max<int64_t>(1, ((int64_t)1 << 30) / A.nF);
+      // grid x = (plane, frame) pairs of this window, y = W segments (or spans), z = row bands;
+      // x stays within 2^32 work-items (kMaxBlocksX blocks of SB_BLEND_THREADS)
+      if (A.nF > sb::kMaxBlocksX)
+        return fail(SB_EGEOM, "a launch window of %d frames exceeds %lld blocks", A.nF,
+                    (long long)sb::kMaxBlocksX);
+      const int64_t max_planes = std::max<int64_t>(1, sb::kMaxBlocksX / A.nF);
       for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
         const int64_t np = std::min(max_planes, planes - p0);
         A.plane0 = (int32_t)p0;

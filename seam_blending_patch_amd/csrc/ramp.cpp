@@ -306,9 +306,14 @@ extern "C" int vae_tile_ramp_blend(const void *const *tiles, const int64_t grid[
       for (size_t c = c0; c < c1; ++c)
         A.t.chunk[c - c0] = sb::ramp_pack((uint32_t)chunks[c].p0, (uint32_t)chunks[c].k0, (uint32_t)chunks[c].cnt);
       A.t.chunk[c1 - c0] = sb::ramp_pack((uint32_t)chunks[c1 - 1].p1, 0, 1);
-      const dim3 g((unsigned)planes, (unsigned)(c1 - c0), (unsigned)b0);
-      hipError_t e = sb_launch_ramp(A, dtype, vec16 ? 1 : 0, g, lds, st);
-      if (e != hipSuccess) return failf(SB_ELAUNCH, "ramp blend launch failed: %s", hipGetErrorString(e));
+      // grid x = planes, in launches of at most kMaxBlocksX (2^32 work-items)
+      for (int64_t p0 = 0; p0 < planes; p0 += sb::kMaxBlocksX) {
+        A.plane0 = p0;
+        const dim3 g((unsigned)std::min<int64_t>(sb::kMaxBlocksX, planes - p0), (unsigned)(c1 - c0),
+                     (unsigned)b0);
+        hipError_t e = sb_launch_ramp(A, dtype, vec16 ? 1 : 0, g, lds, st);
+        if (e != hipSuccess) return failf(SB_ELAUNCH, "ramp blend launch failed: %s", hipGetErrorString(e));
+      }
     }
     s0 = s1;
   }

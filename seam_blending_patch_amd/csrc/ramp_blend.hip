@@ -204,7 +204,7 @@ __global__ __launch_bounds__(SB_RAMP_THREADS) void ramp_blend_kernel(const RampA
   extern __shared__ float lds[];
   __shared__ RampTables T;
   constexpr int EB = Elem<DT>::bytes;
-  const int64_t plane = blockIdx.x;
+  const int64_t plane = A.plane0 + blockIdx.x;
   const int c = blockIdx.y;
   const int band = blockIdx.z;
   constexpr uint32_t PM = (1u << kRampPosBits) - 1u;

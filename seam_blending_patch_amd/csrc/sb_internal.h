@@ -35,6 +35,9 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
 constexpr int kMaxAxisTiles = 64;    // tiles per axis
 constexpr int kMaxWindowTiles = 192; // tile pointers per launch window
 constexpr int kMaxBlend = 4096;      // largest clamped blend extent (LDS coefficient tables)
+// largest grid x of the blend and ramp launches: 2^32 work-items in x at up to
+// 256 threads per block
+constexpr int64_t kMaxBlocksX = ((int64_t)1 << 24) - 1;
 
 struct BlendArgs {
   void *out;
@@ -138,6 +141,7 @@ static_assert(sizeof(RampTables) <= 16 * 256, "copied by one block in one pass")
 struct RampArgs {
   RampTables t;
   void *out;
+  int64_t plane0;                        // first (n, c, frame) plane of this launch
   const void *ptr[kMaxWindowTiles];      // tiles of rows [ib, ib + rows): ptr[(i - ib) * n_w + j]
 };
 

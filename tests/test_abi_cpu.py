@@ -197,6 +197,13 @@ def test_sizes_beyond_the_index_range_are_rejected_on_host(sb):
                                      i64([1, 1 << 20, 48]), 1, ctypes.c_void_p(0x900000), None) == -2
     lib.vae_tile_ramp_blend.restype = ctypes.c_int
     assert _ramp_call(lib, (5, 1 << 16, 1 << 16, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32]) == -2
+    # one temporal tile of 2^25 frames: a launch window holds more frames than
+    # the 2^24 - 1 blocks a grid's x extent allows, refused before any launch
+    one = (ctypes.c_void_p * 1)(0x1000)
+    lib.seamblend_last_error.restype = ctypes.c_char_p
+    assert lib.vae_tile_blend_stitch(one, i64([5, 1, 1, 1, 1, 1]), i64([1 << 25, 1, 1]), i64([0, 0, 0]),
+                                     i64([1, 1, 1]), 0, ctypes.c_void_p(0x40000000), None) == -2
+    assert b"frames exceeds" in lib.seamblend_last_error()
 
 
 def test_row_limit_and_blend_extent_beyond_32_bits(sb):

@@ -128,6 +128,13 @@ def test_many_tiles_use_several_launch_windows(sb):
     check(sb, w5, workloads.draw_tiles(w5), "windows-5d")
 
 
+def test_more_planes_than_one_launch_holds(sb):
+    # 2^24 + 3 (n, c) planes of one-element tiles: more blocks than a grid's
+    # x extent takes (2^32 work-items), so the planes go in two launches
+    w = _wl("bf16", [1], [1], 0, 1, C=(1 << 24) + 3)
+    check(sb, w, workloads.draw_tiles(w), "planes")
+
+
 def test_empty_batch_is_a_noop(sb):
     w = _wl("fp16", [32, 32], [32, 32], 8, 24, N=0)
     tiles = [np.zeros(w.tile_shape(0, i, j), np.float16) for i in range(2) for j in range(2)]

@@ -80,6 +80,13 @@ def check(sb, w, what="", misalign=False, out=None):
     return y
 
 
+def test_more_planes_than_one_launch_holds(sb):
+    # 2^24 + 3 planes of one 1x2 tile: more blocks than a grid's x extent
+    # takes, so the planes go in two launches
+    check(sb, RW("planes", "bf16", (1, (1 << 24) + 3), [0], [1], [0], [2], (4, 4), (8, 8), seed=5,
+                 clamp=None), "planes")
+
+
 @pytest.mark.parametrize("name", sorted(W.RAMP_WORKLOADS))
 def test_named_workloads_full_size(sb, name):
     check(sb, W.RAMP_WORKLOADS[name], "workload")
