@@ -314,8 +314,10 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   A.span_k = (int32_t)span_k;
   A.span_w = (int32_t)span_w;
   A.div_Rw = sb::make_fastdiv((uint32_t)Aw.R);
+  // dynamic LDS: the span layout's coefficient tables and column table (the
+  // segment layout forms its coefficients in registers and needs none)
   const size_t lds = span ? (size_t)(span_w + rows_pb) * sizeof(float2) + (size_t)span_k * sizeof(sb::SpanCol)
-                          : (size_t)(ew_max + rows_pb) * sizeof(float2);
+                          : 0;
   hipStream_t st = (hipStream_t)stream;
   const int64_t n_wseg = span ? n_spans : 2 * Aw.n - 1;
 
@@ -476,6 +478,8 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
   if ((int64_t)a.chunks2 * 256 >= ((int64_t)1 << 32)) return fail(SB_EGEOM, "plane too large");
   a.div_C = sb::make_fastdiv((uint32_t)std::max(a.C, 1));
   a.div_Cg = sb::make_fastdiv((uint32_t)std::max(a.Cg, 1));
+  a.div_P = sb::make_fastdiv((uint32_t)a.P);
+  a.div_G = sb::make_fastdiv((uint32_t)a.G);
   P.ws_bytes = (size_t)shape[0] * groups * n_patches * cpp * 4 * sizeof(float); // (count, m, M2, K_g)
   if (P.ws_bytes == 0) P.ws_bytes = 16;
   return SB_OK;

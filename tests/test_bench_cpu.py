@@ -84,34 +84,34 @@ def _counter_csv(path, rows):
 
 def test_traffic_record_from_counter_runs(tmp_path):
     """Dispatches grouped by (kernel, grid) in launch order, averaged per
-    dispatch, scaled by the 256 MiB copy, and matched to the benchmark's
-    launches; the file records the sources' hashes."""
-    bench = _bench_module()
+    dispatch, scaled by the 256 MiB copy, and matched to the launches of one
+    profile mode of the benchmark; the file records the sources' hashes and
+    keeps the records of other modes."""
+    from benchkit import traffic
     cfg = workloads.CONFIGS[4]
-    n_extra = len(bench.RAMP_NAMES) + len(workloads.ENCODE_BLEND_WORKLOADS)
-    kernels = ([("sb::blend_stitch_kernel", 1), ("sb::gn_stats_kernel", 2), ("sb::gn_norm_kernel", 3)]
-               + [(f"sb::extra_{k}", 10 + k) for k in range(n_extra)])
+    kernels = [("sb::blend_stitch_kernel", 1), ("sb::gn_stats_kernel", 2), ("sb::gn_norm_kernel", 3)]
     for counter, scale in (("FETCH_SIZE", 0.5), ("WRITE_SIZE", 1.0)):
         rows, d = [], 0
-        for rep in range(2):  # two dispatches of every launch, values 100 and 300 KiB
-            for name, grid in kernels:
+        for name, grid in kernels:  # each call's launches together, as the profile mode makes them
+            for rep in range(2):  # two dispatches of every launch, values 100 and 300 KiB
                 d += 1
                 # a counter split over two instances of the same dispatch is summed
                 rows += [(d, name, grid, 1, counter, (100 + 200 * rep) / 2),
                          (d, name, grid, 1, counter, (100 + 200 * rep) / 2)]
-            d += 1
-            rows.append((d, "__amd_rocclr_copyBuffer", 99, 1, counter, 262144 * scale))
+        d += 1
+        rows.append((d, "__amd_rocclr_copyBuffer", 99, 1, counter, 262144 * scale))
         rows.append((d + 1, "torch_fill", 7, 1, counter, 5.0))
         _counter_csv(str(tmp_path / counter / "run" / "run_counter_collection.csv"), rows)
     out = tmp_path / "traffic.json"
-    bench.write_traffic(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"), 4, path=str(out))
+    json.dump({"launches": {"ramp:other": {"kept": True}}}, open(out, "w"))
+    traffic.write_traffic(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"), "config4", path=str(out))
     rec = json.load(open(out))
-    assert rec["calibration"]["fetch_scale"] == pytest.approx(2.0)
-    assert rec["calibration"]["write_scale"] == pytest.approx(1.0)
-    names = list(rec["launches"])
-    assert names[:3] == ["config4-blend", "config4-gn-stats", "config4-gn-norm"]
-    assert len(names) == 3 + n_extra
+    assert rec["launches"]["ramp:other"] == {"kept": True}
     blend = rec["launches"]["config4-blend"]
+    assert blend["calibration"]["fetch_scale"] == pytest.approx(2.0)
+    assert blend["calibration"]["write_scale"] == pytest.approx(1.0)
+    assert [n for n in rec["launches"] if n.startswith("config4")] == [
+        "config4-blend", "config4-gn-stats", "config4-gn-norm"]
     assert blend["dispatches"] == 2
     assert blend["fetch_kib_per_dispatch"] == pytest.approx(200.0)
     assert blend["hbm_bytes_per_launch"] == pytest.approx(200 * 1024 * 2.0 + 200 * 1024)
@@ -120,6 +120,39 @@ def test_traffic_record_from_counter_runs(tmp_path):
     assert blend["algorithmic_bytes_per_launch"] == (w.tile_elems() + out_elems) * 2
     gn = cfg.groupnorm
     assert rec["launches"]["config4-gn-norm"]["algorithmic_bytes_per_launch"] == 2 * 2 * int(np.prod(gn.shape))
-    for r in rec["launches"].values():
-        for f, h in r["sources_sha256"].items():
-            assert os.path.exists(os.path.join(ROOT, f)) and len(h) == 64
+    for name, r in rec["launches"].items():
+        if name.startswith("config4"):
+            for f, h in r["sources_sha256"].items():
+                assert os.path.exists(os.path.join(ROOT, f)) and len(h) == 64
+
+
+def test_kernel_trace_summary(tmp_path):
+    """Per (kernel, grid): dispatch count and average / min / max duration."""
+    from benchkit import traffic
+    d = tmp_path / "kt" / "run"
+    os.makedirs(d)
+    with open(d / "run_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Grid_Size_X,Grid_Size_Y,Grid_Size_Z,Start_Timestamp,End_Timestamp\n")
+        f.write("sb::a,10,1,1,1000,3000\n" "sb::b,5,1,1,4000,5000\n" "sb::a,10,1,1,6000,10000\n")
+    md = traffic.summarize_trace(str(tmp_path / "kt"), "t", "cmd")
+    assert "| `sb::a` | 10x1x1 | 2 | 3.00 | 2.00 | 4.00 |" in md
+    assert "| `sb::b` | 5x1x1 | 1 | 1.00 | 1.00 | 1.00 |" in md
+
+
+def test_probe_library_checks_its_arguments_on_host():
+    """The streaming probe refuses bad sizes and pointers before any launch."""
+    import ctypes
+
+    import benchkit
+    if not os.path.exists(benchkit.LIB):
+        pytest.skip("probe library not built")
+    L = benchkit.lib()
+    f = L.benchkit_stream
+    assert f(None, 1024, None, 0, 0x1000, 4, 0, 0, None) == -1          # null source
+    assert f(0x10000, 1000, None, 0, 0x1000, 4, 0, 0, None) == -1       # not a multiple of 16
+    assert f(0x10000, 1024, None, 512, 0x1000, 4, 0, 0, None) == -1     # writes without a destination
+    assert f(0x10000, 1024, 0x20000, 2048, 0x1000, 4, 0, 0, None) == -1  # writes more than it reads
+    assert f(0x10000, 1024, 0x20008, 512, 0x1000, 4, 0, 0, None) == -1  # misaligned destination
+    assert f(0x10000, 1024, None, 0, 0x1000, 3, 0, 0, None) == -1       # no such shape
+    assert f(0x10000, 16 << 32, None, 0, 0x1000, 1, 0, 0, None) == -1   # grid beyond 2^32 work-items
+    del ctypes

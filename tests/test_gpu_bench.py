@@ -1,7 +1,8 @@
 """The benchmark's JSON line on the GPU: one short run of the default workload
 (a few steps, a short CPU baseline, no extra rows) must print the contract's
 fields, a roofline that is its own achieved / peak, and a bit-exact blend and
-in-tolerance GroupNorm against the oracle on the same run's output."""
+in-tolerance GroupNorm against the oracle on the same run's output, for the
+step and for each of the five workloads' rows."""
 from __future__ import annotations
 
 import json
@@ -22,7 +23,8 @@ def test_bench_line_contract():
     print("[bench] short default run", file=sys.stderr, flush=True)
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "5", "--warmup", "2",
                         "--flushed-reps", "2", "--no-extra", "--cpu-min-seconds", "0.1",
-                        "--cpu-single-seconds", "0"], capture_output=True, text=True, timeout=110)
+                        "--cpu-single-seconds", "0", "--probe-reps", "3"], capture_output=True, text=True,
+                       timeout=200)
     assert r.returncode == 0, r.stderr[-2000:]
     line = json.loads(r.stdout.strip().splitlines()[-1])
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
@@ -40,3 +42,13 @@ def test_bench_line_contract():
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
     assert line["parity"]["blend_mismatches"] == 0
     assert line["parity"]["groupnorm_out_of_tol"] == 0
+    assert line["parity"]["groupnorm_over_literal_1e-2"] >= 0
+    # every workload at full size, in the launch configuration timed, against the oracle
+    assert sorted(line["configs"]) == ["1", "2", "3", "4", "5"]
+    for k, row in line["configs"].items():
+        assert row["blend"]["mismatches"] == 0, k
+        assert row["blend"]["frac"] == pytest.approx(row["blend"]["GBps"] / 8000.0)
+        assert 0 < row["blend"]["ceiling_us"]
+        if "groupnorm" in row:
+            assert row["groupnorm"]["out_of_tol"] == 0, k
+    assert "groupnorm" in line["configs"]["4"] and "groupnorm" not in line["configs"]["2"]
