@@ -396,12 +396,6 @@ def main():
         gn_bytes = 0
     torch.cuda.synchronize()
 
-    # Two events per timed step, before and after the blend launch; a step's
-    # GroupNorm time runs from its after-blend event to the next step's first
-    # event (one more event closes the last step).  A third event after
-    # GroupNorm, back to back with the next step's first, measured 4.3 us of
-    # extra wall time per step with default events, whose system-scope fence
-    # the timing events here skip.
     def step(ev=None):
         if ev is not None:
             ev[0].record()
@@ -411,18 +405,31 @@ def main():
         if has_gn:
             gn()
 
+    # The timed region: exactly K steps between two synchronisations, with
+    # nothing but the step's own launches in it.
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # Then the same K steps again with two events per step, before and after
+    # the blend launch, to split the step's time between its parts; a step's
+    # GroupNorm time runs from its after-blend event to the next step's first
+    # event (one more event closes the last step).  The events add a little
+    # wall time of their own, which is why the timed region above has none.
     evs = [[TimingEvent(torch) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    te0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     evs[-1][2].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    evented_ms_per_step = (time.perf_counter() - te0) * 1e3 / args.steps
     blend_ms = [e[0].elapsed_time(e[1]) for e in evs]
     gn_ms = ([evs[k][1].elapsed_time(evs[k + 1][0]) for k in range(len(evs) - 1)]
              + [evs[-1][1].elapsed_time(evs[-1][2])]) if has_gn else [0.0]
@@ -432,8 +439,9 @@ def main():
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     blend_gbs = blend_bytes / (blend_avg_us * 1e-6) / 1e9
     gn_gbs = gn_bytes / (gn_avg_us * 1e-6) / 1e9 if has_gn else None
-    print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; blend {blend_avg_us:.1f} us "
-          f"({blend_gbs:.0f} GB/s), groupnorm {gn_avg_us:.1f} us", file=sys.stderr, flush=True)
+    print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step ({evented_ms_per_step * 1e3:.1f} with "
+          f"events); blend {blend_avg_us:.1f} us ({blend_gbs:.0f} GB/s), groupnorm {gn_avg_us:.1f} us",
+          file=sys.stderr, flush=True)
 
     # The GroupNorm's traffic streamed by the plain probes in the step's place:
     # the same blend, then a read of |x| (as the statistics pass) and a copy of
@@ -628,6 +636,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": blend_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": blend_gbs / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "blend_stitch_kernel", "launch_us": blend_avg_us},
+        "evented_ms_per_step": evented_ms_per_step,
         "parts": {"blend": {"bytes": blend_bytes, "us": blend_avg_us, "GBps": blend_gbs, "traffic": traffic},
                   "groupnorm": {"bytes": gn_bytes, "us": gn_avg_us, "GBps": gn_gbs, "traffic": gn_traffic,
                                 "after_blend_ceiling": after_blend}},

@@ -231,6 +231,18 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
     const int64_t cap = (((int64_t)1 << 31) - 1) / EB;
     A.off32 = (mh <= cap / std::max<int64_t>(mw, 1) && mh <= cap / std::max<int64_t>(Aw.L, 1)) ? 1 : 0;
   }
+  {
+    // nontemporal output stores when the call's traffic (every tile read,
+    // the output written) is under half the 256 MB last-level cache
+    // (in double: only a size class is wanted, and sums of extreme extents
+    // would overflow 64-bit integers)
+    double st = 0, sh = 0, sw = 0;
+    for (int64_t k = 0; k < At.n; ++k) st += (double)At.ext[k];
+    for (int64_t k = 0; k < Ah.n; ++k) sh += (double)Ah.ext[k];
+    for (int64_t k = 0; k < Aw.n; ++k) sw += (double)Aw.ext[k];
+    const double traffic = (st * sh * sw + (double)At.L * Ah.L * Aw.L) * (double)planes * EB;
+    A.nt_store = traffic < (double)(128 << 20) ? 1 : 0;
+  }
   // Rows per block.  Each block pays a fixed start-up (argument loads, seam
   // coefficient tables, a barrier), so blocks are made as large as the
   // problem allows while still giving every CU several blocks: about

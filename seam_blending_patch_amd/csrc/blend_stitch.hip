@@ -53,9 +53,11 @@
 #ifndef SB_BLEND_NT
 #define SB_BLEND_NT 1 // nontemporal hints on tile loads (each tile element is read once)
 #endif
-#ifndef SB_BLEND_NT_STORE
-#define SB_BLEND_NT_STORE 0 // nontemporal hints on output stores (measured slower: L2 write-combining helps)
-#endif
+// Output stores carry nontemporal hints only when the whole call moves less
+// than about half the 256 MB last-level cache (a host choice, the NTS
+// template parameter): measured on the 64.5 MB 2048x2048 workload, 12% faster
+// back to back and 7% after a cache flush; on the 375 MB and 524 MB ones plain
+// stores are 9-14% faster (L2 write-combining helps there).
 #ifndef SB_BLEND_THREADS
 #define SB_BLEND_THREADS 256
 #endif
@@ -162,7 +164,7 @@ struct Run {
 // a handful of integer operations.  OFF is the offset type: uint32_t when the
 // host has checked that every offset stays below 2^31 bytes (the loads then
 // take a block-uniform base plus a 32-bit lane offset), int64_t otherwise.
-template <int DT, int VB, bool HS, bool WS, bool TS, class OFF>
+template <int DT, int VB, bool HS, bool WS, bool TS, class OFF, bool NTS>
 __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
@@ -237,7 +239,7 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
       if (!b.ok[k]) continue;
       char *dst = R.o + b.od[k];
       if constexpr (!HS && !WS && !TS) {
-        vstore<VB, SB_BLEND_NT_STORE>(dst, b.m[k]);
+        vstore<VB, NTS>(dst, b.m[k]);
       } else if constexpr (DT != DT_F32 && VB == 16) {
         // packed pairs of 16-bit elements
         constexpr int NW = Vec<VB>::NW;
@@ -287,7 +289,7 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
 #pragma unroll
           for (int w = 0; w < NW; ++w) S.w[w] = crossfade2<DT>(Sp.w[w], S.w[w], ta, tb);
         }
-        vstore<VB, SB_BLEND_NT_STORE>(dst, S);
+        vstore<VB, NTS>(dst, S);
       } else {
         float2 chh = make_float2(0.f, 0.f);
         if constexpr (HS) chh = coefficients_r(b.yy[k], R.eh, R.rh);
@@ -333,7 +335,7 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
 #pragma unroll
           for (int e = 0; e < V; ++e) S[e] = crossfade<DT>(Sp[e], S[e], R.ct);
         }
-        vstore<VB, SB_BLEND_NT_STORE>(dst, pack<DT, VB>(S));
+        vstore<VB, NTS>(dst, pack<DT, VB>(S));
       }
     }
   };
@@ -346,7 +348,7 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
 
 // One work item: output frame bx of the (plane, frame) range, W segment by,
 // row band bz.
-template <int DT, int VB, class OFF>
+template <int DT, int VB, class OFF, bool NTS>
 __device__ __forceinline__ void blend_item(const BlendArgs &A, uint32_t bx, uint32_t by, uint32_t bz) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
@@ -466,26 +468,26 @@ __device__ __forceinline__ void blend_item(const BlendArgs &A, uint32_t bx, uint
 
     const int cls = (ts ? 4 : 0) | (hs ? 2 : 0) | (wseam ? 1 : 0);
     switch (cls) {
-      case 0: run_rows<DT, VB, false, false, false, OFF>(R, tid, nthr); break;
-      case 1: run_rows<DT, VB, false, true, false, OFF>(R, tid, nthr); break;
-      case 2: run_rows<DT, VB, true, false, false, OFF>(R, tid, nthr); break;
-      case 3: run_rows<DT, VB, true, true, false, OFF>(R, tid, nthr); break;
-      case 4: run_rows<DT, VB, false, false, true, OFF>(R, tid, nthr); break;
-      case 5: run_rows<DT, VB, false, true, true, OFF>(R, tid, nthr); break;
-      case 6: run_rows<DT, VB, true, false, true, OFF>(R, tid, nthr); break;
-      default: run_rows<DT, VB, true, true, true, OFF>(R, tid, nthr); break;
+      case 0: run_rows<DT, VB, false, false, false, OFF, NTS>(R, tid, nthr); break;
+      case 1: run_rows<DT, VB, false, true, false, OFF, NTS>(R, tid, nthr); break;
+      case 2: run_rows<DT, VB, true, false, false, OFF, NTS>(R, tid, nthr); break;
+      case 3: run_rows<DT, VB, true, true, false, OFF, NTS>(R, tid, nthr); break;
+      case 4: run_rows<DT, VB, false, false, true, OFF, NTS>(R, tid, nthr); break;
+      case 5: run_rows<DT, VB, false, true, true, OFF, NTS>(R, tid, nthr); break;
+      case 6: run_rows<DT, VB, true, false, true, OFF, NTS>(R, tid, nthr); break;
+      default: run_rows<DT, VB, true, true, true, OFF, NTS>(R, tid, nthr); break;
     }
     yo += yl1 - yl;
   }
 }
 
-template <int DT, int VB, class OFF>
+template <int DT, int VB, class OFF, bool NTS>
 __global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_kernel(const BlendArgs A) {
   // Blocks are dispatched in reverse: the last row band and the last frames
   // first.  Row bands further down and later frames are the ones that meet row
   // and frame seams (up to 8 reads per output vector), so the blocks left for
   // the end of the grid are mostly plain copies, which shortens the drain.
-  blend_item<DT, VB, OFF>(A, gridDim.x - 1 - blockIdx.x, gridDim.y - 1 - blockIdx.y, gridDim.z - 1 - blockIdx.z);
+  blend_item<DT, VB, OFF, NTS>(A, gridDim.x - 1 - blockIdx.x, gridDim.y - 1 - blockIdx.y, gridDim.z - 1 - blockIdx.z);
 }
 
 
@@ -561,7 +563,7 @@ __device__ __forceinline__ void span_rows(const SpanRun &R, const SpanCol *cols,
       if (!ok[k]) continue;
       char *dst = R.o + (int64_t)yy[k] * R.opitch + (int64_t)xs[k] * EB;
       if (!HS && !TS && !ws[k]) {
-        vstore<VB, SB_BLEND_NT_STORE>(dst, m[k]);
+        vstore<VB, false>(dst, m[k]);
         continue;
       }
       float2 chh = make_float2(0.f, 0.f);
@@ -608,7 +610,7 @@ __device__ __forceinline__ void span_rows(const SpanRun &R, const SpanCol *cols,
 #pragma unroll
         for (int e = 0; e < V; ++e) S[e] = crossfade<DT>(Sp[e], S[e], R.ct);
       }
-      vstore<VB, SB_BLEND_NT_STORE>(dst, pack<DT, VB>(S));
+      vstore<VB, false>(dst, pack<DT, VB>(S));
     }
   }
 }
@@ -743,8 +745,13 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) void blend_span_kernel(const Blen
 
 template <int DT, int VB>
 static void launch_blend_typed(const sb::BlendArgs &a, dim3 grid, dim3 b, size_t lds, hipStream_t st) {
-  if (a.off32) hipLaunchKernelGGL((sb::blend_stitch_kernel<DT, VB, uint32_t>), grid, b, lds, st, a);
-  else hipLaunchKernelGGL((sb::blend_stitch_kernel<DT, VB, int64_t>), grid, b, lds, st, a);
+  if (a.nt_store) {
+    if (a.off32) hipLaunchKernelGGL((sb::blend_stitch_kernel<DT, VB, uint32_t, true>), grid, b, lds, st, a);
+    else hipLaunchKernelGGL((sb::blend_stitch_kernel<DT, VB, int64_t, true>), grid, b, lds, st, a);
+  } else {
+    if (a.off32) hipLaunchKernelGGL((sb::blend_stitch_kernel<DT, VB, uint32_t, false>), grid, b, lds, st, a);
+    else hipLaunchKernelGGL((sb::blend_stitch_kernel<DT, VB, int64_t, false>), grid, b, lds, st, a);
+  }
 }
 
 hipError_t sb_launch_blend(const sb::BlendArgs &a, int dtype, int vec16, dim3 grid, size_t lds,

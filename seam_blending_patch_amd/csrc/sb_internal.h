@@ -54,6 +54,7 @@ struct BlendArgs {
   int32_t span_k;                   // span layout: tile columns per span (0: segment layout)
   int32_t span_w;                   // span layout: widest span in elements (LDS table length)
   int32_t off32;                    // every tile and output offset a block forms is below 2^31 bytes
+  int32_t nt_store;                 // output stores with nontemporal hints (calls moving < 128 MB)
   FastDiv div_nF, div_Rt, div_Rh, div_Rw;
 };
 
