@@ -322,6 +322,8 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
     const int64_t nrb = (Ah.L + rows_pb - 1) / rows_pb;
     rows_pb = (Ah.L + nrb - 1) / nrb;
   }
+  // row bands go on a grid axis of at most kMaxBlocksYZ blocks
+  rows_pb = std::max<int64_t>(rows_pb, (Ah.L + sb::kMaxBlocksYZ - 1) / sb::kMaxBlocksYZ);
   A.rows_per_block = (int32_t)rows_pb;
   A.span_k = (int32_t)span_k;
   A.span_w = (int32_t)span_w;
@@ -330,6 +332,9 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   // segment layout forms its coefficients in registers and needs none)
   const size_t lds = span ? (size_t)(span_w + rows_pb) * sizeof(float2) + (size_t)span_k * sizeof(sb::SpanCol)
                           : 0;
+  if (lds > 65536)
+    return fail(SB_EGEOM, "output of %lld rows needs %zu bytes of LDS per block in the narrow-seam layout",
+                (long long)Ah.L, lds);
   hipStream_t st = (hipStream_t)stream;
   const int64_t n_wseg = span ? n_spans : 2 * Aw.n - 1;
 
@@ -376,8 +381,12 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
         const int64_t np = std::min(max_planes, planes - p0);
         A.plane0 = (int32_t)p0;
         const dim3 grid((unsigned)(np * A.nF), (unsigned)n_wseg, (unsigned)row_blocks);
+        // the segment kernel takes (segments, bands, planes x frames) when the
+        // last fits the grid's z extent (see blend_stitch_kernel)
+        A.order = (!span && np * A.nF <= sb::kMaxBlocksYZ) ? 1 : 0;
+        const dim3 g = A.order ? dim3(grid.y, grid.z, grid.x) : grid;
         hipError_t e = span ? sb_launch_blend_span(A, dtype, vec16 ? 1 : 0, grid, lds, st)
-                            : sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid, lds, st);
+                            : sb_launch_blend(A, dtype, vec16 ? 1 : 0, g, lds, st);
         if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
       }
       i0 = i1;

@@ -80,12 +80,41 @@ __device__ __forceinline__ Stat chan_merge(const Stat &a, const Stat &b) {
   return o;
 }
 
-__device__ __forceinline__ Stat shfl_down_stat(const Stat &s, int o) {
+// The statistics of lane l + O (O = 1, 2, 4 or 8, inside the lane's row of
+// 16), read with a DPP row shift (a VALU operand modifier, no LDS trip).
+template <int O> __device__ __forceinline__ Stat dpp_down_stat(const Stat &s) {
+  constexpr int ctrl = 0x100 + O; // row_shl:O -- lane i reads lane i + O of its row
   Stat t;
-  t.n = (uint32_t)__shfl_down((int)s.n, o, 64);
-  t.mean = __shfl_down(s.mean, o, 64);
-  t.m2 = __shfl_down(s.m2, o, 64);
+  t.n = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s.n, ctrl, 0xf, 0xf, false);
+  t.mean = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s.mean), ctrl, 0xf, 0xf, false));
+  t.m2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s.m2), ctrl, 0xf, 0xf, false));
   return t;
+}
+
+// One level of the wavefront merge tree inside rows: lane l (l a multiple of
+// 2O) takes in lane l + O.
+template <int O> __device__ __forceinline__ void tree_level(Stat &st, int lane) {
+  const Stat t = dpp_down_stat<O>(st);
+  if ((lane & (2 * O - 1)) == 0) st = chan_merge(st, t);
+}
+
+__device__ __forceinline__ Stat readlane_stat(const Stat &s, int l) {
+  return Stat{(uint32_t)__builtin_amdgcn_readlane((int)s.n, l),
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s.mean), l)),
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s.m2), l))};
+}
+
+// The whole wavefront's statistics by the fixed tree lane l += lane l + o for
+// o = 1, 2, 4, 8 (DPP, inside rows of 16), then rows 0+1, 2+3 and the two
+// halves (read lanes 0, 16, 32, 48).  Returned in every lane.
+__device__ __forceinline__ Stat wave_merge(Stat st, int lane) {
+  tree_level<1>(st, lane);
+  tree_level<2>(st, lane);
+  tree_level<4>(st, lane);
+  tree_level<8>(st, lane);
+  const Stat lo = chan_merge(readlane_stat(st, 0), readlane_stat(st, 16));
+  const Stat hi = chan_merge(readlane_stat(st, 32), readlane_stat(st, 48));
+  return chan_merge(lo, hi);
 }
 
 #ifndef SB_GN_STATS_BATCH
@@ -154,41 +183,56 @@ __device__ __forceinline__ void accumulate_batch(Stat &st, const Vec<VB> (&v)[kS
   st = chan_merge(st, Stat{nb, mb, q});
 }
 
+constexpr int kStatsThreads = 64 * kStatsWaves; // threads per pass-1 block (a constant: no launch-argument read)
+
 template <int DT, int VB>
-__global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv div_big,
+__global__ __launch_bounds__(kStatsThreads) void gn_stats_kernel(const GNArgs A, FastDiv div_big,
                                                        FastDiv div_small) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int c = b & (A.CPP - 1);
-  int rest = b >> A.log2CPP;
-  const int np_ = (int)fdiv((uint32_t)rest, A.div_P); // rest = (n * G + g) * P + p
-  const int p = rest - np_ * A.P;
-  const int n = (int)fdiv((uint32_t)np_, A.div_G);
-  const int g = np_ - n * A.G;
+  // Every launch argument the first loads depend on, read at entry and pinned
+  // in scalar registers by an empty asm, so that they arrive in one round of
+  // scalar loads (left alone, the compiler loads the patch-length divisor
+  // through a block-dependent address, a second dependent round).
+  uint32_t l2cpp = A.log2CPP, nP = A.P, nG = A.G, nbig = A.n_big, lbig = A.len_big, lsmall = A.len_small;
+  uint32_t dPm = A.div_P.m, dPs = A.div_P.s, dGm = A.div_G.m, dGs = A.div_G.s;
+  uint32_t bm = div_big.m, bs = div_big.s, sm = div_small.m, ss = div_small.s;
+  uint32_t Cc = A.C, Cg = A.Cg, Lx = A.L;
+  int64_t inner = A.inner, mid = A.mid, S = A.S;
+  asm volatile("" : "+s"(l2cpp), "+s"(nP), "+s"(nG), "+s"(nbig), "+s"(lbig), "+s"(lsmall), "+s"(dPm),
+               "+s"(dPs), "+s"(dGm), "+s"(dGs), "+s"(bm), "+s"(bs), "+s"(sm), "+s"(ss), "+s"(Cc), "+s"(Cg),
+               "+s"(Lx), "+s"(inner), "+s"(mid), "+s"(S));
+  const uint32_t cpp = 1u << l2cpp;
+  const int c = b & (cpp - 1);
+  const uint32_t rest = (uint32_t)b >> l2cpp;
+  const uint32_t np_ = (__umulhi(rest, dPm) + rest) >> dPs; // rest = (n * G + g) * P + p
+  const int p = (int)(rest - np_ * nP);
+  const int n = (int)((__umulhi(np_, dGm) + np_) >> dGs);
+  const int g = (int)(np_ - (uint32_t)n * nG);
 
-  const bool big = p < A.n_big;
-  const int len = big ? A.len_big : A.len_small;
-  const int start = big ? p * A.len_big : A.n_big * A.len_big + (p - A.n_big) * A.len_small;
-  const uint32_t runv = (uint32_t)(((int64_t)len * A.inner) / V);
-  const FastDiv dv = big ? div_big : div_small;
-  const uint32_t totalv = (uint32_t)((int64_t)A.Cg * A.mid * runv);
-  const uint32_t per = (totalv + A.CPP - 1) / A.CPP;
+  const bool big = (uint32_t)p < nbig;
+  const int len = big ? lbig : lsmall;
+  const int start = big ? p * lbig : nbig * lbig + (p - nbig) * lsmall;
+  const uint32_t runv = (uint32_t)(((int64_t)len * inner) / V);
+  const FastDiv dv{runv, big ? bm : sm, big ? bs : ss};
+  const uint32_t totalv = (uint32_t)((int64_t)Cg * mid * runv);
+  const uint32_t per = (totalv + cpp - 1) >> l2cpp; // chunks per patch are a power of two
   const uint32_t q0 = (uint32_t)c * per;
   const uint32_t q1 = min(q0 + per, totalv);
-  const int64_t row = (int64_t)A.L * A.inner; // elements between consecutive runs
-  const int64_t g0 = ((int64_t)n * A.C + (int64_t)g * A.Cg) * A.S;
-  const char *gbase = (const char *)A.x + (g0 + (int64_t)start * A.inner) * EB;
+  const int64_t row = (int64_t)Lx * inner; // elements between consecutive runs
+  const int64_t g0 = ((int64_t)n * Cc + (int64_t)g * Cg) * S;
+  const char *gbase = (const char *)A.x + (g0 + (int64_t)start * inner) * EB;
 
-  // Vectors q0 + tid + k * blockDim.x, in batches of kStatsBatch whose loads
+  // Vectors q0 + tid + k * kStatsThreads, in batches of kStatsBatch whose loads
   // are issued together.
   Vec<VB> v[kStatsBatch];
   bool ok[kStatsBatch];
   auto load_batch = [&](uint32_t base) {
 #pragma unroll
     for (int u = 0; u < kStatsBatch; ++u) {
-      const uint32_t q = base + u * blockDim.x;
+      const uint32_t q = base + u * kStatsThreads;
       ok[u] = q < q1;
       if (ok[u]) {
         const uint32_t r = fdiv(q, dv);
@@ -200,7 +244,7 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
   // The first batch is issued before the group shift is read, so the two
   // share one memory latency; every later batch finds K_g in a register.
   Stat st{0u, 0.f, 0.f};
-  const uint32_t step = blockDim.x * kStatsBatch;
+  const uint32_t step = kStatsThreads * kStatsBatch;
   uint32_t base = q0 + tid;
   load_batch(base);
   const float K = group_shift<DT>(A.x, g0, (int64_t)A.Cg * A.S);
@@ -209,19 +253,14 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const GNArgs A, FastDiv d
     load_batch(base);
     accumulate_batch<DT, VB>(st, v, ok, K);
   }
-  // wavefront tree, lane l merges lane l + o
   const int lane = tid & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const Stat t = shfl_down_stat(st, o);
-    if ((lane & (2 * o - 1)) == 0 && lane + o < 64) st = chan_merge(st, t);
-  }
-  __shared__ Stat s_w[4];
+  st = wave_merge(st, lane);
+  __shared__ Stat s_w[kStatsWaves];
   if (lane == 0) s_w[tid >> 6] = st;
   __syncthreads();
   if (tid == 0) {
     Stat m = s_w[0];
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = chan_merge(m, s_w[w]);
+    for (int w = 1; w < kStatsWaves; ++w) m = chan_merge(m, s_w[w]);
     float4 *dst = reinterpret_cast<float4 *>(A.part) + b;
     *dst = make_float4(__uint_as_float(m.n), m.mean, m.m2, K);
   }
@@ -349,7 +388,7 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   // alone while x is in flight (measured: each order is the faster one on its
   // side of the threshold the host sets).
   const int lane = tid & 63;
-  const int K = A.P * A.CPP;
+  const int K = A.P * A.CPP; // partials of the group (lane l holds patch l / CPP, chunk l % CPP)
   float4 src = make_float4(0.f, 0.f, 0.f, 0.f);
   uint32_t graw, braw;
   Vec<VB> xs[kNormUnroll];
@@ -375,27 +414,45 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   const float gam = A.gamma ? widen<DT>(graw) : 1.0f;
   const float bet = A.beta ? widen<DT>(braw) : 0.0f;
 
-  // merge the group's partials
+  // merge the group's partials with the fixed tree of wave_merge
   Stat st{__float_as_uint(src.x), src.y, src.z};
-  const float kg = src.w; // the group shift K_g (the same in every partial of the group)
-  const float Kg = __shfl(kg, 0, 64);
+  // the group shift K_g (the same in every partial of the group; lane 0 holds partial 0)
+  const float Kg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src.w), 0));
   const bool writer = A.patch_stats != nullptr && chunk == 0 && ch == g * A.Cg && tid < 64;
-  if (writer && A.CPP == 1 && lane < A.P) {
+  const int cppl = A.CPP; // lanes per patch
+  if (writer && cppl == 1 && lane < A.P) {
     float *d = A.patch_stats + (ng * A.P + lane) * 3;
     d[0] = (float)st.n; d[1] = st.n > 0 ? Kg + st.mean : 0.f; d[2] = st.m2;
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const Stat t = shfl_down_stat(st, o);
-    if ((lane & (2 * o - 1)) == 0 && lane + o < 64) st = chan_merge(st, t);
-    if (writer && 2 * o == A.CPP && (lane & (A.CPP - 1)) == 0 && (lane >> A.log2CPP) < A.P) {
-      float *d = A.patch_stats + (ng * A.P + (lane >> A.log2CPP)) * 3;
-      d[0] = (float)st.n; d[1] = st.n > 0 ? Kg + st.mean : 0.f; d[2] = st.m2;
-    }
+  // the fixed tree of wave_merge; after the level at which 2o == CPP, lane
+  // p * CPP holds patch p, which the writer records
+  auto record = [&](const Stat &v, int p) {
+    float *d = A.patch_stats + (ng * A.P + p) * 3;
+    d[0] = (float)v.n; d[1] = v.n > 0 ? Kg + v.mean : 0.f; d[2] = v.m2;
+  };
+  auto record_rows = [&](int o) {
+    if (writer && 2 * o == cppl && (lane & (cppl - 1)) == 0 && (lane >> A.log2CPP) < A.P)
+      record(st, lane >> A.log2CPP);
+  };
+  tree_level<1>(st, lane);
+  record_rows(1);
+  tree_level<2>(st, lane);
+  record_rows(2);
+  tree_level<4>(st, lane);
+  record_rows(4);
+  tree_level<8>(st, lane);
+  record_rows(8);
+  const Stat lo = chan_merge(readlane_stat(st, 0), readlane_stat(st, 16));
+  const Stat hi = chan_merge(readlane_stat(st, 32), readlane_stat(st, 48));
+  if (writer && cppl == 32 && lane == 0) {
+    record(lo, 0);
+    if (A.P > 1) record(hi, 1);
   }
-  const float cnt = (float)(uint32_t)__shfl((int)st.n, 0, 64);
-  const float mean = __shfl(st.mean, 0, 64);
-  const float m2 = __shfl(st.m2, 0, 64);
+  st = chan_merge(lo, hi);
+  if (writer && cppl == 64 && lane == 0) record(st, 0);
+  const float cnt = (float)st.n;
+  const float mean = st.mean;
+  const float m2 = st.m2;
   const float var = m2 / cnt;
   const float rstd = 1.0f / sqrtf(var + A.eps);
   const float a = rstd * gam;
@@ -427,7 +484,7 @@ static hipError_t launch_gn(const GNArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((gn_stats_rows_kernel<DT, VB>), dim3((unsigned)((int64_t)a.N * a.G * a.CPP)),
                        dim3(kRowsThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((gn_stats_kernel<DT, VB>), dim3(blocks1), dim3(256), 0, st, a, db, ds);
+    hipLaunchKernelGGL((gn_stats_kernel<DT, VB>), dim3(blocks1), dim3(kStatsThreads), 0, st, a, db, ds);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // pass 2: (chunks of a plane, planes) with at most kMaxGridY planes per

@@ -38,6 +38,7 @@ constexpr int kMaxBlend = 4096;      // largest clamped blend extent (LDS coeffi
 // largest grid x of the blend and ramp launches: 2^32 work-items in x at up to
 // 256 threads per block
 constexpr int64_t kMaxBlocksX = ((int64_t)1 << 24) - 1;
+constexpr int64_t kMaxBlocksYZ = 65535; // largest grid extent in y and z
 
 struct BlendArgs {
   void *out;
@@ -55,6 +56,7 @@ struct BlendArgs {
   int32_t span_w;                   // span layout: widest span in elements (LDS table length)
   int32_t off32;                    // every tile and output offset a block forms is below 2^31 bytes
   int32_t nt_store;                 // output stores with nontemporal hints (calls moving < 128 MB)
+  int32_t order;                    // segment kernel grid: 0 = (pf, seg, band), 1 = (seg, band, pf)
   FastDiv div_nF, div_Rt, div_Rh, div_Rw;
 };
 
@@ -74,6 +76,7 @@ struct SpanCol {
 // GroupNorm launch arguments
 // ---------------------------------------------------------------------------
 constexpr int kMaxPatches = 64;
+constexpr int kStatsWaves = 4; // waves of a pass-1 block (per-patch layout)
 #ifndef SB_GN_NORM_UNROLL
 #define SB_GN_NORM_UNROLL 4
 #endif
@@ -88,7 +91,7 @@ struct GNArgs {
   float *patch_stats; // optional [N][G][P][3]
   int32_t N, C, G, Cg;
   int64_t S;          // spatial elements per channel
-  int32_t P, CPP, log2CPP;
+  int32_t P, CPP, log2CPP;  // patches; pass-1 chunks (and partials) per patch, a power of two
   int32_t L;          // extent of the split axis
   int64_t inner;      // elements per step along the split axis
   int64_t mid;        // product of the spatial extents before the split axis
