@@ -145,6 +145,34 @@ bool vector_runs(const AxisLayout &A, const std::vector<Run> &el, int64_t V, std
   return true;
 }
 
+// The same runs on 128-byte lines (G positions): a line that straddles a
+// change takes every tile with weight anywhere in it.  Those tiles carry
+// exactly zero weight on the line's positions outside their weighted ranges
+// (the normalised weights and the sums they enter are unchanged), and no two
+// column chunks then share a line of the output or of a tile row, so no line
+// is fetched or written by two blocks.  Returns false when some such tile
+// does not cover the whole line, or a line would take more than
+// kRampMaxCover tiles.
+bool line_runs(const AxisLayout &A, const std::vector<Run> &el, int64_t G, std::vector<Run> &out) {
+  out.clear();
+  size_t r = 0;
+  for (int64_t q0 = 0; q0 < A.L; q0 += G) {
+    const int64_t q1 = std::min(q0 + G, A.L);
+    while (r < el.size() && el[r].p1 <= q0) ++r;
+    int kmin = 1 << 30, kmax = -1;
+    for (size_t t = r; t < el.size() && el[t].p0 < q1; ++t) {
+      kmin = std::min(kmin, el[t].k0);
+      kmax = std::max(kmax, el[t].k0 + el[t].cnt);
+    }
+    if (kmax - kmin > sb::kRampMaxCover) return false;
+    for (int k = kmin; k < kmax; ++k)
+      if (A.o[k] > q0 || A.o[k] + A.s[k] < q1) return false;
+    if (!out.empty() && out.back().k0 == kmin && out.back().cnt == kmax - kmin) out.back().p1 = q1;
+    else out.push_back(Run{q0, q1, kmin, kmax - kmin});
+  }
+  return true;
+}
+
 // split runs into pieces of at most `single` (one tile) or `multi` (several)
 // positions, each a whole number of V-position vectors
 void split_runs(const std::vector<Run> &runs, int64_t single, int64_t multi, int64_t V, std::vector<Run> &out) {
@@ -223,9 +251,27 @@ extern "C" int vae_tile_ramp_blend(const void *const *tiles, const int64_t grid[
   if (vec16) vec16 = vector_runs(W, wr_el, V16, wr);
   const int64_t V = vec16 ? V16 : 1;
   if (!vec16) wr = wr_el;
+  // Column chunks on whole 128-byte lines when every tile origin along W is
+  // on a line (then a line of the output is a line of every tile too) and
+  // every straddling line can take the tiles of both sides: FLUX.1 at 1600 px
+  // drops from +6.6% to +2.5% HBM traffic over the algorithmic bytes.  With
+  // origins off the line grid, a chunk edge on an output line still splits a
+  // tile line, and the union lines add zero-weight reads (2752x1536 layout:
+  // +26.8% against +9.6% on 16-byte vectors), so those keep vector chunks.
+  int64_t gran = V;
+  {
+    const int64_t G = 128 / EB;
+    bool on_lines = vec16;
+    for (int64_t j = 0; j < n_w && on_lines; ++j) on_lines = W.o[j] % G == 0;
+    std::vector<Run> lr;
+    if (on_lines && line_runs(W, wr_el, G, lr)) {
+      wr = lr;
+      gran = G;
+    }
+  }
 
   std::vector<Run> chunks;
-  split_runs(wr, sb::kRampSingleVecs * V, sb::kRampMultiCols, V, chunks);
+  split_runs(wr, sb::kRampSingleVecs * V, sb::kRampMultiCols, gran, chunks);
 
   sb::RampArgs A;
   std::memset(&A, 0, sizeof A);

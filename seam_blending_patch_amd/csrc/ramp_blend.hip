@@ -248,7 +248,9 @@ __global__ __launch_bounds__(SB_RAMP_THREADS) void ramp_blend_kernel(const RampA
         const int ti = i0 + i, tj = j0 + j;
         // element (y, x) of the output at tile element (y - oh, x - ow)
         const int64_t base = (plane * T.sh[ti] - T.oh[ti]) * (int64_t)T.sw[tj] - T.ow[tj];
-        B.tile[i][j] = uniform((const char *)A.ptr[uniform((ti - T.ib) * T.n_w + tj)] + base * EB);
+        // (the index is uniform, so the pointer is a scalar load of the
+        // launch arguments and keeps its global address space)
+        B.tile[i][j] = (const char *)A.ptr[uniform((ti - T.ib) * T.n_w + tj)] + base * EB;
       } else {
         B.tile[i][j] = nullptr;
       }
