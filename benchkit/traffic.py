@@ -15,6 +15,7 @@ duration.
 
     python -m benchkit.traffic traffic {config1..config5|extra} FETCH_DIR WRITE_DIR
     python -m benchkit.traffic trace TRACE_DIR OUT.md "TITLE" "COMMAND"
+    python -m benchkit.traffic table OUT.md
 """
 from __future__ import annotations
 
@@ -180,12 +181,52 @@ def summarize_trace(trace_dir, title, command):
         name = key[0] if len(key[0]) <= 90 else key[0][:87] + "..."
         lines.append(f"| `{name}` | {'x'.join(map(str, key[1]))} | {len(d)} | {sum(d) / len(d):.2f} | "
                      f"{min(d):.2f} | {max(d):.2f} |")
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        lines += ["", "rocprofv3 --stats (per kernel name, all grids together):", "",
+                  "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+        for r in csv.DictReader(open(stats[0])):
+            name = r["Name"] if len(r["Name"]) <= 90 else r["Name"][:87] + "..."
+            lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def pmc_command(what):
+    """The commands that make one profile mode's traffic records."""
+    return (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_FETCH_SIZE_{what} -o run -- "
+            f"python3 bench.py --profile {what} --steps 3 --warmup 1; the same with WRITE_SIZE into "
+            f"gpurun_out/pmc_WRITE_SIZE_{what}; python3 -m benchkit.traffic traffic {what} "
+            f"gpurun_out/pmc_FETCH_SIZE_{what} gpurun_out/pmc_WRITE_SIZE_{what}")
+
+
+def traffic_table(path=None):
+    """Markdown table of traffic.json: per launch, counted HBM bytes against
+    the algorithmic bytes, with the counter readings and copy calibration."""
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path))
+    lines = ["# HBM traffic per launch (rocprofv3 PMC FETCH_SIZE, WRITE_SIZE)", "", rec["what"] + ".", "",
+             "Commands (from the repository root, on one MI355X, one counter per run, each under "
+             "`timeout -s KILL 120`), for each profile mode `<w>` of config1..config5 and extra:", "", "```",
+             "cd /tmp && export TMPDIR=/tmp", pmc_command("<w>"), "```", "",
+             "| launch | kernel | fetch KiB | write KiB | fetch scale | HBM bytes | algorithmic bytes | excess |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name, r in rec["launches"].items():
+        k = r["kernel"] if len(r["kernel"]) <= 60 else r["kernel"][:57] + "..."
+        lines.append(f"| {name} | `{k}` | {r['fetch_kib_per_dispatch']:.1f} | {r['write_kib_per_dispatch']:.1f} | "
+                     f"{r['calibration']['fetch_scale']:.3f} | {r['hbm_bytes_per_launch']:.0f} | "
+                     f"{r['algorithmic_bytes_per_launch']} | {100 * r['excess']:+.1f}% |")
     return "\n".join(lines) + "\n"
 
 
 def main(argv):
     if len(argv) >= 4 and argv[0] == "traffic":
-        write_traffic(argv[2], argv[3], argv[1])
+        write_traffic(argv[2], argv[3], argv[1], command=pmc_command(argv[1]))
+    elif len(argv) >= 2 and argv[0] == "table":
+        md = traffic_table()
+        with open(argv[1], "w") as f:
+            f.write(md)
+        print(md)
     elif len(argv) >= 5 and argv[0] == "trace":
         md = summarize_trace(argv[1], argv[3], argv[4])
         with open(argv[2], "w") as f:
