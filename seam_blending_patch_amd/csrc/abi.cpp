@@ -209,6 +209,9 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
       A.ext[a][k] = (int32_t)X.ext[k];
       if (X.e[k] > sb::kMaxBlend)
         return fail(SB_EGEOM, "clamped blend extent %lld exceeds %d", (long long)X.e[k], sb::kMaxBlend);
+      // the seam's reciprocal, rounded once from float64 as the kernel's
+      // coefficient formula requires
+      A.rcp[a][k] = X.e[k] > 0 ? (float)(1.0 / (double)X.e[k]) : 0.f;
       if (a == 2) ew_max = std::max(ew_max, X.e[k]);
     }
   }
@@ -243,9 +246,9 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
     const double traffic = (st * sh * sw + (double)At.L * Ah.L * Aw.L) * (double)planes * EB;
     A.nt_store = traffic < (double)(128 << 20) ? 1 : 0;
   }
-  // Rows per block.  Each block pays a fixed start-up (argument loads, seam
-  // coefficient tables, a barrier), so blocks are made as large as the
-  // problem allows while still giving every CU several blocks: about
+  // Rows per block.  Each block pays a fixed start-up (argument loads; in the
+  // span layout also its coefficient tables and a barrier), so blocks are made
+  // as large as the problem allows while still giving every CU several blocks: about
   // total / (cus * SB_BLEND_BLOCKS_PER_CU) vectors in the widest W segment,
   // clamped to [1024, 8192]; the band height is then aligned to the row seams
   // or balanced over the rows (below).
@@ -369,25 +372,43 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
       const int64_t Y0 = i0 * Ah.R, Y1 = (i1 == Ah.n) ? Ah.L : i1 * Ah.R;
       A.F0 = (int32_t)F0; A.nF = (int32_t)(F1 - F0);
       A.Y0 = (int32_t)Y0; A.nY = (int32_t)(Y1 - Y0);
-      A.div_nF = sb::make_fastdiv((uint32_t)A.nF);
       const int64_t row_blocks = (A.nY + rows_pb - 1) / rows_pb;
-      // grid x = (plane, frame) pairs of this window, y = W segments (or spans), z = row bands;
-      // x stays within 2^32 work-items (kMaxBlocksX blocks of SB_BLEND_THREADS)
-      if (A.nF > sb::kMaxBlocksX)
-        return fail(SB_EGEOM, "a launch window of %d frames exceeds %lld blocks", A.nF,
-                    (long long)sb::kMaxBlocksX);
-      const int64_t max_planes = std::max<int64_t>(1, sb::kMaxBlocksX / A.nF);
-      for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
-        const int64_t np = std::min(max_planes, planes - p0);
-        A.plane0 = (int32_t)p0;
-        const dim3 grid((unsigned)(np * A.nF), (unsigned)n_wseg, (unsigned)row_blocks);
-        // the segment kernel takes (segments, bands, planes x frames) when the
-        // last fits the grid's z extent (see blend_stitch_kernel)
-        A.order = (!span && np * A.nF <= sb::kMaxBlocksYZ) ? 1 : 0;
-        const dim3 g = A.order ? dim3(grid.y, grid.z, grid.x) : grid;
-        hipError_t e = span ? sb_launch_blend_span(A, dtype, vec16 ? 1 : 0, grid, lds, st)
-                            : sb_launch_blend(A, dtype, vec16 ? 1 : 0, g, lds, st);
-        if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
+      if (span) {
+        // span kernel: grid x = (plane, frame) pairs of this window, y = spans,
+        // z = row bands; x stays within 2^32 work-items (kMaxBlocksX blocks)
+        A.div_nF = sb::make_fastdiv((uint32_t)A.nF);
+        if (A.nF > sb::kMaxBlocksX)
+          return fail(SB_EGEOM, "a launch window of %d frames exceeds %lld blocks", A.nF,
+                      (long long)sb::kMaxBlocksX);
+        const int64_t max_planes = std::max<int64_t>(1, sb::kMaxBlocksX / A.nF);
+        for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
+          const int64_t np = std::min(max_planes, planes - p0);
+          A.plane0 = (int32_t)p0;
+          const dim3 grid((unsigned)(np * A.nF), (unsigned)n_wseg, (unsigned)row_blocks);
+          hipError_t e = sb_launch_blend_span(A, dtype, vec16 ? 1 : 0, grid, lds, st);
+          if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
+        }
+      } else {
+        // segment kernel: grid (W segments, row bands, (plane, frame) pairs),
+        // at most kMaxBlocksYZ pairs per launch: the window's frames go in
+        // ranges of at most that many, and planes as many as fit beside them
+        for (int64_t fa = F0; fa < F1; fa += sb::kMaxBlocksYZ) {
+          const int64_t nf = std::min<int64_t>(sb::kMaxBlocksYZ, F1 - fa);
+          A.F0 = (int32_t)fa;
+          A.nF = (int32_t)nf;
+          A.div_nF = sb::make_fastdiv((uint32_t)nf);
+          const int64_t max_planes = std::max<int64_t>(1, sb::kMaxBlocksYZ / nf);
+          for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
+            const int64_t np = std::min(max_planes, planes - p0);
+            A.plane0 = (int32_t)p0;
+            A.g_seg = (int32_t)n_wseg;
+            A.g_band = (int32_t)row_blocks;
+            A.g_pf = (int32_t)(np * nf);
+            const dim3 grid((unsigned)n_wseg, (unsigned)row_blocks, (unsigned)(np * nf));
+            hipError_t e = sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid, lds, st);
+            if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
+          }
+        }
       }
       i0 = i1;
     }

@@ -30,9 +30,7 @@
 // Work layout.  Along W every tile j contributes a seam segment (its first
 // min(e_w, crop) columns) and a body segment (the rest of its crop); along H
 // likewise per tile row; along T per frame.  A block owns one output frame of
-// one (n, c) plane, one W segment and a band of output rows (the frame index
-// varies fastest over the grid, so blocks resident together mix frames with
-// and without frame seams, spreading the heavy ones), so the column
+// one (n, c) plane, one W segment and a band of output rows, so the column
 // tile, the column seam class, the temporal tile and the frame seam class are
 // block-uniform; the band is split at tile-row seam boundaries into runs whose
 // row class is block-uniform too.  Each run therefore executes one specialised
@@ -151,11 +149,19 @@ struct Run {
   int64_t opitch;                // bytes per output row
   int y0, y1;                    // local rows [y0, y1) of tile row i
   int x0, wv;                    // first local column of the segment, vectors per row
-  float inv_wv;
   int eh, ew;                    // row and column seam extents (row / column seams)
-  float rh, rw;                  // their reciprocals, recip_of(eh) and recip_of(ew)
+  float rh, rw;                  // their reciprocals, fp32(1/eh) and fp32(1/ew)
   float2 ct;                     // frame coefficient (frame seams)
 };
+
+// q = n / d and n - q * d for 0 <= n < 2^24, d >= 1 uniform: the hardware
+// reciprocal's quotient is within one of the exact one, and two compares fix it.
+__device__ __forceinline__ int2 divmod_small(int n, int d, float rd) {
+  int q = (int)((float)n * rd);
+  q -= (q * d > n) ? 1 : 0;
+  q += ((q + 1) * d <= n) ? 1 : 0;
+  return make_int2(q, n - q * d);
+}
 
 // Walks the run's (rows x wv) vectors, nthreads apart, U per lane per batch.
 // Each lane keeps its position (row r, vector x) and the byte offsets of that
@@ -172,14 +178,13 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
   constexpr int U = L >= SB_BLEND_LOADS ? 1 : SB_BLEND_LOADS / L; // output vectors per thread per batch
   const int nrows = R.y1 - R.y0;
   const int wv = R.wv;
-  // first position: tid / wv exactly (the float quotient is within one of it for tid < 2^24)
-  int r = (int)((float)tid * R.inv_wv);
-  r -= (r * wv > tid) ? 1 : 0;
-  r += ((r + 1) * wv <= tid) ? 1 : 0;
-  int x = tid - r * wv;
-  // one step of nthreads vectors: dr rows and dx vectors, plus a carry row when x passes wv
-  const int dr = nthreads / wv;
-  const int dx = nthreads - dr * wv;
+  // first position (tid / wv, tid mod wv) and one step of nthreads vectors:
+  // dr rows and dx vectors, plus a carry row when x passes wv
+  const float rwv = __builtin_amdgcn_rcpf((float)wv);
+  const int2 p0 = divmod_small(tid, wv, rwv);
+  const int2 st = divmod_small(nthreads, wv, rwv);
+  int r = p0.x, x = p0.y;
+  const int dr = st.x, dx = st.y;
   const OFF pj = (OFF)R.pitch_j, pp = (OFF)R.pitch_p, po = (OFF)R.opitch;
   constexpr int VBY = V * EB; // bytes per vector
   const OFF xstep = (OFF)dx * VBY, xwrap = (OFF)wv * VBY;
@@ -346,65 +351,101 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
   }
 }
 
-// One work item: output frame bx of the (plane, frame) range, W segment by,
-// row band bz.
+typedef const __attribute__((address_space(1))) char *GPtr;
+typedef __attribute__((address_space(1))) char *GOut;
+
+struct PtrPair {
+  const char *a, *b; // pointer-table entries k-1 and k
+};
+
+// The tiles the closed form reads for one tile row of a segment: (i,j),
+// (i-1,j), (i,j-1), (i-1,j-1) of chunk tau, then the same in chunk tau-1.
+struct Tiles {
+  const char *m, *u, *l, *c, *pm, *pu, *pl, *pc;
+};
+
+// The launch arguments a block reads before its first tile loads.
+struct Head {
+  int32_t nw, nh, nt, E0, E1, E2, R0, R1, R2, LT, LH, LW, taub, ib, ptr_nh, F0, nF, Y0, nY, plane0, rows_pb;
+  int32_t g_seg, g_band, g_pf;
+  uint32_t nFm, nFs, Rtm, Rts, Rhm, Rhs;
+  char *out;
+};
+
+__device__ __forceinline__ uint32_t fdiv_ms(uint32_t n, uint32_t m, uint32_t s) {
+  return (__umulhi(n, m) + n) >> s;
+}
+
+// One work item: (plane, frame) pf of the launch, W segment sw, row band bz.
 template <int DT, int VB, class OFF, bool NTS>
-__device__ __forceinline__ void blend_item(const BlendArgs &A, uint32_t bx, uint32_t by, uint32_t bz) {
+__device__ __forceinline__ void blend_item(const BlendArgs &A, const Head &H, uint32_t pz, int sw, int bz) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  const int nw = A.n_w, nh = A.n_h, nt = A.n_t;
+  const int tid = threadIdx.x;
+  constexpr int nthr = SB_BLEND_THREADS;
+  const int nw = H.nw, nh = H.nh, nt = H.nt;
 
-  // ---- block-uniform indices: arithmetic on the block index and the fixed
+  // ---- block-uniform indices: arithmetic on the block index and the pinned
   //      argument fields only ----
-  const int sw = by; // x = (plane, frame), y = W segment, z = row band
-  const int j = (sw + 1) >> 1;
+  const uint32_t j = (uint32_t)(sw + 1) >> 1;
   const bool wseam = (sw & 1) != 0;
-  const uint32_t pz = bx;
-  const uint32_t pli = fdiv(pz, A.div_nF);
-  const int64_t plane = (int64_t)A.plane0 + pli;
-  const int f_out = A.F0 + (int)(pz - pli * (uint32_t)A.nF);
-  const int tau = min((int)fdiv((uint32_t)f_out, A.div_Rt), nt - 1);
-  const int f = f_out - tau * A.R[0];
-  const int r0 = (int)bz * A.rows_per_block;
-  const int r1 = min(r0 + A.rows_per_block, A.nY);
-  const int yo0 = A.Y0 + r0, yo1 = A.Y0 + r1;
-  const int ia = min((int)fdiv((uint32_t)yo0, A.div_Rh), nh - 1); // tile row of the first run
+  const uint32_t pli = fdiv_ms(pz, H.nFm, H.nFs);
+  const uint32_t plane = (uint32_t)H.plane0 + pli; // N * C < 2^31
+  const uint32_t f_out = (uint32_t)H.F0 + (pz - pli * (uint32_t)H.nF);
+  const uint32_t tau = min(fdiv_ms(f_out, H.Rtm, H.Rts), (uint32_t)nt - 1);
+  const int f = (int)(f_out - tau * (uint32_t)H.R0);
+  const int r0 = bz * H.rows_pb;
+  const int r1 = min(r0 + H.rows_pb, H.nY);
+  const int yo0 = H.Y0 + r0, yo1 = H.Y0 + r1;
+  const uint32_t ia = min(fdiv_ms((uint32_t)yo0, H.Rhm, H.Rhs), (uint32_t)nh - 1); // first run's tile row
 
-  // ---- the extents and tile pointers of the block's first run, all requested
-  //      at once: every index is clamped into the launch window (tau-1 and
-  //      i-1 never fall below the window's first chunk and tile row), so the
-  //      loads need no branch and share one memory latency; the ones a block
-  //      has no seam for are simply not used ----
-  const int jm = max(j - 1, 0), taum = max(tau - 1, 0), iam = max(ia - 1, 0);
-  const int wj = A.ext[2][j], wjm = A.ext[2][jm];
-  const int tt = A.ext[0][tau], ttm = A.ext[0][taum];
-  const int hia = A.ext[1][ia], hiam = A.ext[1][iam];
-  const char *const *P = (const char *const *)A.ptr;
-  auto tile = [&](int tq, int ti, int tj) {
-    return P[((tq - A.taub) * A.ptr_nh + (ti - A.ib)) * nw + tj];
+  // ---- the extents, seam reciprocals and tile pointers of the block's first
+  //      run, all requested at once and pinned, so they arrive in one more
+  //      round of scalar loads.  Tile (tq, ti, tj) of the window is entry
+  //      ((tq - taub) * ptr_nh + (ti - ib)) * nw + tj; the neighbours are
+  //      fixed steps back from (tau, ia, j), taken as zero steps where there
+  //      is none (index 0 along that axis).  Tile columns j-1 and j are
+  //      adjacent entries, loaded as one pair; at j = 0 the first of the pair
+  //      is the entry (or, at entry 0, the argument word) before and is not
+  //      used ----
+  const uint32_t su = ia > 0 ? (uint32_t)nw : 0u;
+  const uint32_t st = tau > 0 ? (uint32_t)(H.ptr_nh * nw) : 0u;
+  const uint32_t jm = j > 0 ? j - 1 : 0u, iam = ia > 0 ? ia - 1 : 0u, taum = tau > 0 ? tau - 1 : 0u;
+  int wj = A.ext[2][j], wjm = A.ext[2][jm];
+  int tt = A.ext[0][tau], ttm = A.ext[0][taum];
+  int hia = A.ext[1][ia], hiam = A.ext[1][iam];
+  float rw = A.rcp[2][j], rt = A.rcp[0][tau], rh0 = A.rcp[1][ia];
+  // byte offset of entry b's pair (entries b-1, b) from the start of the table
+  const char *const tab = (const char *)A.ptr - sizeof(void *);
+  auto pair = [&](uint32_t b) { return *(const PtrPair *)(tab + (size_t)(b * (uint32_t)sizeof(void *))); };
+  const uint32_t b0 = ((tau - (uint32_t)H.taub) * (uint32_t)H.ptr_nh + (ia - (uint32_t)H.ib)) * (uint32_t)nw + j;
+  auto tiles_of_row = [&](uint32_t b, uint32_t sui) {
+    const PtrPair lm = pair(b), cu = pair(b - sui), plm = pair(b - st), pcu = pair(b - st - sui);
+    return Tiles{lm.b, cu.b, lm.a, cu.a, plm.b, pcu.b, plm.a, pcu.a};
   };
-  struct Tiles {
-    const char *m, *u, *l, *c, *pm, *pu, *pl, *pc;
-  };
-  auto tiles_of_row = [&](int i) {
-    const int im = max(i - 1, 0);
-    return Tiles{tile(tau, i, j),     tile(tau, im, j),     tile(tau, i, jm),     tile(tau, im, jm),
-                 tile(taum, i, j),    tile(taum, im, j),    tile(taum, i, jm),    tile(taum, im, jm)};
-  };
-  Tiles T = tiles_of_row(ia);
+  Tiles T = tiles_of_row(b0, su);
+  {
+    // pinned as global-address-space pointers: a generic pointer coming out
+    // of the asm would turn every tile load into a flat load
+    GPtr m = (GPtr)T.m, u = (GPtr)T.u, l = (GPtr)T.l, c = (GPtr)T.c;
+    GPtr pm = (GPtr)T.pm, pu = (GPtr)T.pu, pl = (GPtr)T.pl, pc = (GPtr)T.pc;
+    asm volatile("" : "+s"(wj), "+s"(wjm), "+s"(tt), "+s"(ttm), "+s"(hia), "+s"(hiam), "+s"(rw), "+s"(rt),
+                 "+s"(rh0), "+s"(m), "+s"(u), "+s"(l), "+s"(c), "+s"(pm), "+s"(pu), "+s"(pl), "+s"(pc));
+    T = Tiles{(const char *)m,  (const char *)u,  (const char *)l,  (const char *)c,
+              (const char *)pm, (const char *)pu, (const char *)pl, (const char *)pc};
+  }
 
   // ---- W segment: tile column j, seam or body ----
   const int wp = j > 0 ? wjm : 0;
-  const int ew = j > 0 ? min(A.E[2], min(wp, wj)) : 0;
-  const int cw = j < nw - 1 ? A.R[2] : wj;
+  const int ew = j > 0 ? min(H.E2, min(wp, wj)) : 0;
+  const int cw = j < nw - 1 ? H.R2 : wj;
   const int ews = min(ew, cw);
   const int x0 = wseam ? 0 : ews;
   const int x1 = wseam ? ews : cw;
 
   // ---- frame: temporal tile tau, local frame f ----
   const int tp = tau > 0 ? ttm : 0;
-  const int et = tau > 0 ? min(A.E[0], min(tp, tt)) : 0;
+  const int et = tau > 0 ? min(H.E0, min(tp, tt)) : 0;
   const bool ts = f < et;
   const int fp = tp - et + f; // frame of chunk tau-1 blended into frame f
 
@@ -412,24 +453,28 @@ __device__ __forceinline__ void blend_item(const BlendArgs &A, uint32_t bx, uint
 
   // seam coefficients are formed per vector from (position, extent,
   // reciprocal); only the frame coefficient is block-uniform
-  const float rw = wseam ? recip_of(ew) : 0.f;
-  const float2 ct = ts ? coefficients(f, et) : make_float2(0.f, 0.f);
+  const float2 ct = ts ? coefficients_r(f, et, rt) : make_float2(0.f, 0.f);
+  // (plane, frame) slices of the chunks tau and tau-1 read here, in frames
+  const uint64_t sfm = (uint64_t)plane * (uint32_t)tt + (uint32_t)f;
+  const uint64_t sfp = (uint64_t)plane * (uint32_t)tp + (uint32_t)fp;
 
   // ---- runs of rows with one tile row and one row class ----
-  int cur = ia;                // tile row whose extents and tiles are loaded
+  int cur = (int)ia;           // tile row whose extents and tiles are loaded
   int hi = hia, hp = hiam;     // its extent and the one above (clamped at row 0)
+  float rh = rh0;              // fp32(1/e) of its row seam
   int yo = yo0;
   while (yo < yo1) {
-    const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
-    if (i != cur) { // the band crosses into the next tile row
-      cur = i;
+    const int i = min((int)fdiv_ms((uint32_t)yo, H.Rhm, H.Rhs), nh - 1);
+    if (i != cur) { // the band crosses into the next tile row (i > 0)
       hp = A.ext[1][i - 1];
       hi = A.ext[1][i];
-      T = tiles_of_row(i);
+      rh = A.rcp[1][i];
+      T = tiles_of_row(b0 + (uint32_t)(i - (int)ia) * (uint32_t)nw, (uint32_t)nw);
+      cur = i;
     }
-    const int ybase = i * A.R[1];
-    const int eh = i > 0 ? min(A.E[1], min(hp, hi)) : 0;
-    const int chh = i < nh - 1 ? A.R[1] : hi;
+    const int ybase = i * H.R1;
+    const int eh = i > 0 ? min(H.E1, min(hp, hi)) : 0;
+    const int chh = i < nh - 1 ? H.R1 : hi;
     const int ehs = min(eh, chh);
     const int yl = yo - ybase;
     const bool hs = yl < ehs;
@@ -437,31 +482,32 @@ __device__ __forceinline__ void blend_item(const BlendArgs &A, uint32_t bx, uint
 
     Run R;
     const int u = hp - eh, l = wp - ew;
-    // plane, frame and neighbour-tail offsets folded into the tile bases
-    const int64_t pj = (int64_t)wj * EB, pp = (int64_t)wp * EB;
-    R.pitch_j = pj;
-    R.pitch_p = pp;
-    R.m = T.m + ((plane * tt + f) * hi) * pj;
+    // plane, frame and neighbour-tail offsets folded into the tile bases, in
+    // elements: rows of (tile row i or i-1) x (tile column j or j-1)
+    const uint64_t rm = sfm * (uint32_t)hi, ru = sfm * (uint32_t)hp + (uint32_t)u;
+    R.pitch_j = (int64_t)wj * EB;
+    R.pitch_p = (int64_t)wp * EB;
+    R.m = T.m + rm * (uint32_t)wj * EB;
     R.u = R.l = R.c = R.pm = R.pu = R.pl = R.pc = nullptr;
-    if (hs) R.u = T.u + ((plane * tt + f) * hp + u) * pj;
-    if (wseam) R.l = T.l + ((plane * tt + f) * hi) * pp + (int64_t)l * EB;
-    if (hs && wseam) R.c = T.c + ((plane * tt + f) * hp + u) * pp + (int64_t)l * EB;
+    if (hs) R.u = T.u + ru * (uint32_t)wj * EB;
+    if (wseam) R.l = T.l + (rm * (uint32_t)wp + (uint32_t)l) * EB;
+    if (hs && wseam) R.c = T.c + (ru * (uint32_t)wp + (uint32_t)l) * EB;
     if (ts) {
-      R.pm = T.pm + ((plane * tp + fp) * hi) * pj;
-      if (hs) R.pu = T.pu + ((plane * tp + fp) * hp + u) * pj;
-      if (wseam) R.pl = T.pl + ((plane * tp + fp) * hi) * pp + (int64_t)l * EB;
-      if (hs && wseam) R.pc = T.pc + ((plane * tp + fp) * hp + u) * pp + (int64_t)l * EB;
+      const uint64_t qm = sfp * (uint32_t)hi, qu = sfp * (uint32_t)hp + (uint32_t)u;
+      R.pm = T.pm + qm * (uint32_t)wj * EB;
+      if (hs) R.pu = T.pu + qu * (uint32_t)wj * EB;
+      if (wseam) R.pl = T.pl + (qm * (uint32_t)wp + (uint32_t)l) * EB;
+      if (hs && wseam) R.pc = T.pc + (qu * (uint32_t)wp + (uint32_t)l) * EB;
     }
-    R.opitch = (int64_t)A.LW * EB;
-    R.o = (char *)A.out + (((plane * A.LT + f_out) * A.LH + ybase) * (int64_t)A.LW +
-                           (int64_t)j * A.R[2] + x0) * EB;
+    R.opitch = (int64_t)H.LW * EB;
+    R.o = H.out + ((((uint64_t)plane * (uint32_t)H.LT + (uint32_t)f_out) * (uint32_t)H.LH + (uint32_t)ybase) *
+                       (uint32_t)H.LW + (uint32_t)(j * H.R2 + x0)) * EB;
     R.y0 = yl;
     R.y1 = yl1;
     R.x0 = x0;
     R.wv = (x1 - x0) / V;
-    R.inv_wv = 1.0f / (float)R.wv;
     R.eh = eh;
-    R.rh = hs ? recip_of(eh) : 0.f;
+    R.rh = rh;
     R.ew = ew;
     R.rw = rw;
     R.ct = ct;
@@ -483,22 +529,42 @@ __device__ __forceinline__ void blend_item(const BlendArgs &A, uint32_t bx, uint
 
 template <int DT, int VB, class OFF, bool NTS>
 __global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_kernel(const BlendArgs A) {
-  // Blocks are dispatched in reverse: the last row band and the last frames
-  // first.  Row bands further down and later frames are the ones that meet row
-  // and frame seams (up to 8 reads per output vector), so the blocks left for
-  // the end of the grid are mostly plain copies, which shortens the drain.
-  // With order 1 the grid is (W segments, row bands, (plane, frame)): the
-  // blocks dispatched together cover whole output rows of one frame, so the
-  // concurrent reads and writes stay within a few frames (video workload:
-  // 66.0 -> 63.3 us back to back, 68.5 -> 66.2 us after a flush); order 0
-  // ((plane, frame), W segments, row bands) is the fallback when the planes
-  // and frames of a launch exceed the grid's z extent.
-  if (A.order)
-    blend_item<DT, VB, OFF, NTS>(A, gridDim.z - 1 - blockIdx.z, gridDim.x - 1 - blockIdx.x, gridDim.y - 1 - blockIdx.y);
-  else
-    blend_item<DT, VB, OFF, NTS>(A, gridDim.x - 1 - blockIdx.x, gridDim.y - 1 - blockIdx.y, gridDim.z - 1 - blockIdx.z);
+  // Every launch argument the block decode and the first run read, read at
+  // entry and pinned in scalar registers by empty asm statements, so that they
+  // arrive in one round of scalar loads; left alone, the compiler spreads them
+  // over a chain of dependent rounds between branches (about nine before the
+  // first tile load), which took most of a small block's life.  The grid
+  // extents come from the arguments too: gridDim and blockDim would be more
+  // loads of their own.
+  Head H;
+  H.nw = A.n_w; H.nh = A.n_h; H.nt = A.n_t;
+  H.E0 = A.E[0]; H.E1 = A.E[1]; H.E2 = A.E[2];
+  H.R0 = A.R[0]; H.R1 = A.R[1]; H.R2 = A.R[2];
+  H.LT = A.LT; H.LH = A.LH; H.LW = A.LW;
+  H.taub = A.taub; H.ib = A.ib; H.ptr_nh = A.ptr_nh;
+  H.F0 = A.F0; H.nF = A.nF; H.Y0 = A.Y0; H.nY = A.nY; H.plane0 = A.plane0; H.rows_pb = A.rows_per_block;
+  H.g_seg = A.g_seg; H.g_band = A.g_band; H.g_pf = A.g_pf;
+  H.nFm = A.div_nF.m; H.nFs = A.div_nF.s; H.Rtm = A.div_Rt.m; H.Rts = A.div_Rt.s;
+  H.Rhm = A.div_Rh.m; H.Rhs = A.div_Rh.s;
+  GOut out = (GOut)A.out; // pinned in the global address space (see blend_item)
+  asm volatile("" : "+s"(H.nw), "+s"(H.nh), "+s"(H.nt), "+s"(H.E0), "+s"(H.E1), "+s"(H.E2), "+s"(H.R0),
+               "+s"(H.R1), "+s"(H.R2), "+s"(H.LT), "+s"(H.LH), "+s"(H.LW), "+s"(H.taub), "+s"(H.ib),
+               "+s"(H.ptr_nh), "+s"(H.F0));
+  asm volatile("" : "+s"(H.nF), "+s"(H.Y0), "+s"(H.nY), "+s"(H.plane0), "+s"(H.rows_pb), "+s"(H.g_seg),
+               "+s"(H.g_band), "+s"(H.g_pf), "+s"(H.nFm), "+s"(H.nFs), "+s"(H.Rtm), "+s"(H.Rts), "+s"(H.Rhm),
+               "+s"(H.Rhs), "+s"(out));
+  H.out = (char *)out;
+  // The grid is (W segments, row bands, (plane, frame)), taken in reverse:
+  // the last row band and the last frames first.  Row bands further down and
+  // later frames are the ones that meet row and frame seams (up to 8 reads per
+  // output vector), so the blocks left for the end of the grid are mostly
+  // plain copies, which shortens the drain; and the blocks dispatched together
+  // cover whole output rows of one frame, so the concurrent reads and writes
+  // stay within a few frames (video workload: 66.0 -> 63.3 us back to back,
+  // 68.5 -> 66.2 us after a flush, against (plane, frame) fastest).
+  blend_item<DT, VB, OFF, NTS>(A, H, (uint32_t)(H.g_pf - 1) - blockIdx.z, H.g_seg - 1 - (int)blockIdx.x,
+                               H.g_band - 1 - (int)blockIdx.y);
 }
-
 
 // ---------------------------------------------------------------------------
 // Span layout, for narrow seams.  When every W segment is only a few vectors

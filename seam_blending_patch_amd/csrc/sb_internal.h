@@ -44,6 +44,7 @@ struct BlendArgs {
   void *out;
   const void *ptr[kMaxWindowTiles]; // window tiles [(tau - taub)][(i - ib)][j]
   int32_t ext[3][kMaxAxisTiles];    // extents per axis (t, h, w), global tile index
+  float rcp[3][kMaxAxisTiles];      // fp32(1/e) of the seam between tiles k-1 and k per axis (0: no seam)
   int32_t n_t, n_h, n_w;
   int32_t E[3], R[3];
   int32_t LT, LH, LW;               // full output extents
@@ -56,7 +57,7 @@ struct BlendArgs {
   int32_t span_w;                   // span layout: widest span in elements (LDS table length)
   int32_t off32;                    // every tile and output offset a block forms is below 2^31 bytes
   int32_t nt_store;                 // output stores with nontemporal hints (calls moving < 128 MB)
-  int32_t order;                    // segment kernel grid: 0 = (pf, seg, band), 1 = (seg, band, pf)
+  int32_t g_seg, g_band, g_pf;      // segment kernel grid: W segments, row bands, (plane, frame) pairs
   FastDiv div_nF, div_Rt, div_Rh, div_Rw;
 };
 

@@ -197,12 +197,14 @@ def test_sizes_beyond_the_index_range_are_rejected_on_host(sb):
                                      i64([1, 1 << 20, 48]), 1, ctypes.c_void_p(0x900000), None) == -2
     lib.vae_tile_ramp_blend.restype = ctypes.c_int
     assert _ramp_call(lib, (5, 1 << 16, 1 << 16, 1, 1, 2), [0, 0, 0, 16], [1, 32, 32, 32]) == -2
-    # one temporal tile of 2^25 frames: a launch window holds more frames than
-    # the 2^24 - 1 blocks a grid's x extent allows, refused before any launch
-    one = (ctypes.c_void_p * 1)(0x1000)
+    # one temporal tile of 2^25 frames in the narrow-seam layout (two 8-wide
+    # tile columns, 4-column seam): its grid's x extent takes the window's
+    # frames, and 2^25 exceed the 2^24 - 1 blocks it allows, refused before any
+    # launch (the segment layout takes any frame count, in ranges)
+    two = (ctypes.c_void_p * 2)(0x1000, 1 << 40)
     lib.seamblend_last_error.restype = ctypes.c_char_p
-    assert lib.vae_tile_blend_stitch(one, i64([5, 1, 1, 1, 1, 1]), i64([1 << 25, 1, 1]), i64([0, 0, 0]),
-                                     i64([1, 1, 1]), 0, ctypes.c_void_p(0x40000000), None) == -2
+    assert lib.vae_tile_blend_stitch(two, i64([5, 1, 1, 1, 1, 2]), i64([1 << 25, 1, 8, 8]), i64([0, 0, 4]),
+                                     i64([1, 1, 8]), 0, ctypes.c_void_p(1 << 41), None) == -2
     assert b"frames exceeds" in lib.seamblend_last_error()
 
 

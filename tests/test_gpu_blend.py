@@ -135,6 +135,15 @@ def test_more_planes_than_one_launch_holds(sb):
     check(sb, w, workloads.draw_tiles(w), "planes")
 
 
+def test_more_plane_frame_pairs_than_one_launch_holds(sb):
+    # 2 planes x 65,630 frames: the segment kernel takes at most 65,535
+    # (plane, frame) pairs per launch (its grid's z extent), so the frames go
+    # in two ranges, one plane per launch in the first; the 8-frame seam at
+    # frames 65,530..65,537 crosses the boundary between the ranges
+    w = _wl("bf16", [4], [8], 0, 8, ndim=5, ext_t=(65540, 100), Et=8, Rt=65530, C=2)
+    check(sb, w, workloads.draw_tiles(w), "plane-frame ranges")
+
+
 def test_empty_batch_is_a_noop(sb):
     w = _wl("fp16", [32, 32], [32, 32], 8, 24, N=0)
     tiles = [np.zeros(w.tile_shape(0, i, j), np.float16) for i in range(2) for j in range(2)]
