@@ -513,11 +513,11 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
   a.CPP = (int32_t)cpp;
   a.log2CPP = 0;
   while ((1 << a.log2CPP) < cpp) a.log2CPP++;
-  a.per2 = 256 * sb::kNormUnroll; // vectors per pass-2 block (256 threads x kNormUnroll)
+  a.per2 = sb::kNormThreads * sb::kNormUnroll; // vectors per pass-2 block
   a.chunks2 = (int32_t)std::max<int64_t>(1, (S / V + a.per2 - 1) / a.per2);
   // pass 2 runs on a (chunks of a plane, planes) grid: 2^32 work-items in x;
   // planes beyond the grid's y extent take further launches
-  if ((int64_t)a.chunks2 * 256 >= ((int64_t)1 << 32)) return fail(SB_EGEOM, "plane too large");
+  if ((int64_t)a.chunks2 * sb::kNormThreads >= ((int64_t)1 << 32)) return fail(SB_EGEOM, "plane too large");
   a.div_C = sb::make_fastdiv((uint32_t)std::max(a.C, 1));
   a.div_Cg = sb::make_fastdiv((uint32_t)std::max(a.Cg, 1));
   a.div_P = sb::make_fastdiv((uint32_t)a.P);

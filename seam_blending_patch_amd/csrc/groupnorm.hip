@@ -363,21 +363,31 @@ __global__ __launch_bounds__(kRowsThreads) void gn_stats_rows_kernel(const GNArg
 
 
 template <int DT, int VB, bool XFIRST>
-__global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
+__global__ __launch_bounds__(kNormThreads) void gn_norm_kernel(const GNArgs A) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
   const int tid = threadIdx.x;
-  const int chunk = blockIdx.x;
-  const uint32_t plane = A.plane0 + blockIdx.y; // < 2^31 (checked on the host)
-  const int n = (int)fdiv(plane, A.div_C);
-  const int ch = (int)(plane - (uint32_t)n * (uint32_t)A.C);
-  const int g = (int)fdiv((uint32_t)ch, A.div_Cg);
-  const int64_t ng = (int64_t)n * A.G + g;
-  const int64_t Sv = A.S / V;
-  const int64_t q0 = (int64_t)chunk * A.per2;
-  const int64_t q1 = min(q0 + A.per2, Sv);
-  const char *xb = (const char *)A.x + (int64_t)plane * A.S * EB;
-  char *yb = (char *)A.out + (int64_t)plane * A.S * EB;
+  const uint32_t chunk = blockIdx.x;
+  // Every launch argument the first loads depend on, read at entry and pinned
+  // in scalar registers, so they arrive in one round of scalar loads (the
+  // block size is a constant, not the implicit argument).
+  uint32_t plane0 = A.plane0, dCm = A.div_C.m, dCs = A.div_C.s, dGm = A.div_Cg.m, dGs = A.div_Cg.s;
+  uint32_t Cc = A.C, Gg = A.G, per = (uint32_t)A.per2, Kp = (uint32_t)(A.P * A.CPP);
+  int64_t S = A.S;
+  asm volatile("" : "+s"(plane0), "+s"(dCm), "+s"(dCs), "+s"(dGm), "+s"(dGs), "+s"(Cc), "+s"(Gg), "+s"(per),
+               "+s"(Kp), "+s"(S));
+  const uint32_t plane = plane0 + blockIdx.y; // < 2^31 (checked on the host)
+  const uint32_t n = (__umulhi(plane, dCm) + plane) >> dCs;
+  const uint32_t ch = plane - n * Cc;
+  const uint32_t g = (__umulhi(ch, dGm) + ch) >> dGs;
+  const uint32_t ng = n * Gg + g;
+  // a channel plane is below 2^31 elements (its group is), so vector indices
+  // within it are 32-bit
+  const uint32_t Sv = (uint32_t)(S / V);
+  const uint32_t q0 = chunk * per;
+  const uint32_t q1 = min(q0 + per, Sv);
+  const char *xb = (const char *)A.x + (uint64_t)plane * (uint64_t)S * EB;
+  char *yb = (char *)A.out + (uint64_t)plane * (uint64_t)S * EB;
 
   // The group's partials (lane l holds patch l / CPP, chunk l % CPP), this
   // channel's gamma and beta, and the block's vectors of x.  gamma and beta
@@ -388,20 +398,20 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   // alone while x is in flight (measured: each order is the faster one on its
   // side of the threshold the host sets).
   const int lane = tid & 63;
-  const int K = A.P * A.CPP; // partials of the group (lane l holds patch l / CPP, chunk l % CPP)
+  const int K = (int)Kp; // partials of the group (lane l holds patch l / CPP, chunk l % CPP)
   float4 src = make_float4(0.f, 0.f, 0.f, 0.f);
   uint32_t graw, braw;
   Vec<VB> xs[kNormUnroll];
   auto load_small = [&]() {
-    if (lane < K) src = reinterpret_cast<const float4 *>(A.part)[ng * K + lane];
+    if (lane < K) src = reinterpret_cast<const float4 *>(A.part)[(uint64_t)ng * (uint32_t)K + lane];
     graw = load_elem<DT>(A.gamma ? A.gamma : A.x, A.gamma ? ch : 0);
     braw = load_elem<DT>(A.beta ? A.beta : A.x, A.beta ? ch : 0);
   };
   auto load_x = [&]() {
 #pragma unroll
     for (int u = 0; u < kNormUnroll; ++u) {
-      const int64_t q = min(q0 + (int64_t)u * blockDim.x + tid, q1 - 1); // q1 > q0: the plane is non-empty
-      xs[u] = vload<VB, SB_GN_NT_LOAD2>(xb + q * V * EB);
+      const uint32_t q = min(q0 + (uint32_t)(u * kNormThreads + tid), q1 - 1); // q1 > q0: the plane is non-empty
+      xs[u] = vload<VB, SB_GN_NT_LOAD2>(xb + (size_t)q * (V * EB));
     }
   };
   if constexpr (XFIRST) {
@@ -421,13 +431,13 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
   const bool writer = A.patch_stats != nullptr && chunk == 0 && ch == g * A.Cg && tid < 64;
   const int cppl = A.CPP; // lanes per patch
   if (writer && cppl == 1 && lane < A.P) {
-    float *d = A.patch_stats + (ng * A.P + lane) * 3;
+    float *d = A.patch_stats + ((size_t)ng * A.P + lane) * 3;
     d[0] = (float)st.n; d[1] = st.n > 0 ? Kg + st.mean : 0.f; d[2] = st.m2;
   }
   // the fixed tree of wave_merge; after the level at which 2o == CPP, lane
   // p * CPP holds patch p, which the writer records
   auto record = [&](const Stat &v, int p) {
-    float *d = A.patch_stats + (ng * A.P + p) * 3;
+    float *d = A.patch_stats + ((size_t)ng * A.P + p) * 3;
     d[0] = (float)v.n; d[1] = v.n > 0 ? Kg + v.mean : 0.f; d[2] = v.m2;
   };
   auto record_rows = [&](int o) {
@@ -459,13 +469,13 @@ __global__ __launch_bounds__(256) void gn_norm_kernel(const GNArgs A) {
 
 #pragma unroll
   for (int u = 0; u < kNormUnroll; ++u) {
-    const int64_t q = q0 + (int64_t)u * blockDim.x + tid;
+    const uint32_t q = q0 + (uint32_t)(u * kNormThreads + tid);
     if (q < q1) {
       float f[V];
       unpack<DT, VB>(xs[u], f);
 #pragma unroll
       for (int k = 0; k < V; ++k) f[k] = fmaf((f[k] - Kg) - mean, a, bet);
-      vstore<VB, SB_GN_NT_STORE>(yb + q * V * EB, pack<DT, VB>(f));
+      vstore<VB, SB_GN_NT_STORE>(yb + (size_t)q * (V * EB), pack<DT, VB>(f));
     }
   }
 }
@@ -495,9 +505,9 @@ static hipError_t launch_gn(const GNArgs &a, hipStream_t st) {
     w.plane0 = (uint32_t)p0;
     const dim3 grid2((unsigned)a.chunks2, (unsigned)std::min<int64_t>(kMaxGridY, planes - p0));
     if (a.x_first)
-      hipLaunchKernelGGL((gn_norm_kernel<DT, VB, true>), grid2, dim3(256), 0, st, w);
+      hipLaunchKernelGGL((gn_norm_kernel<DT, VB, true>), grid2, dim3(kNormThreads), 0, st, w);
     else
-      hipLaunchKernelGGL((gn_norm_kernel<DT, VB, false>), grid2, dim3(256), 0, st, w);
+      hipLaunchKernelGGL((gn_norm_kernel<DT, VB, false>), grid2, dim3(kNormThreads), 0, st, w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -77,11 +77,15 @@ struct SpanCol {
 // GroupNorm launch arguments
 // ---------------------------------------------------------------------------
 constexpr int kMaxPatches = 64;
-constexpr int kStatsWaves = 4; // waves of a pass-1 block (per-patch layout)
+#ifndef SB_GN_STATS_WAVES
+#define SB_GN_STATS_WAVES 4
+#endif
+constexpr int kStatsWaves = SB_GN_STATS_WAVES; // waves of a pass-1 block (per-patch layout)
 #ifndef SB_GN_NORM_UNROLL
 #define SB_GN_NORM_UNROLL 4
 #endif
 constexpr int kNormUnroll = SB_GN_NORM_UNROLL; // vectors per thread in the normalise pass
+constexpr int kNormThreads = 256;             // threads per normalise block
 
 struct GNArgs {
   const void *x;
