@@ -87,6 +87,13 @@ def test_more_planes_than_one_launch_holds(sb):
                  clamp=None), "planes")
 
 
+def test_tall_canvas_of_many_row_bands(sb):
+    # a 310,000-row canvas two vectors wide: about 1,200 row bands of a few
+    # hundred rows over three row segments, two of them single-tile
+    check(sb, RW("tall", "bf16", (1, 1), [0, 150000], [160000, 160000], [0], [16], (4, 4), (8, 8), seed=6),
+          "bands across launches")
+
+
 @pytest.mark.parametrize("name", sorted(W.RAMP_WORKLOADS))
 def test_named_workloads_full_size(sb, name):
     check(sb, W.RAMP_WORKLOADS[name], "workload")
