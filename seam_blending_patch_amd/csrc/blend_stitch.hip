@@ -113,18 +113,14 @@ __device__ __forceinline__ uint32_t crossfade2(uint32_t a, uint32_t b, f32x2 wa,
   return add2<DT>(narrow2<DT>(pa), narrow2<DT>(pb));
 }
 
-__device__ __forceinline__ float2 coefficients(int k, int e) {
-  const double q = (double)k / (double)e;
-  return make_float2((float)(1.0 - q), (float)q);
-}
-
-// The same coefficients without a float64 division per entry: with
-// r = fp32(1/e), the quotient n/e (n = k or e - k, whole numbers) is formed as
-// q0 = n * r, corrected once by the exact fp32 remainder n - q0 * e (one fused
+// The seam coefficients w_b = fp32(k/e) and w_a = fp32(1 - k/e), float64
+// quotients rounded once to fp32, formed without a float64 division: with
+// r = fp32(1/e) (computed on the host from float64, BlendArgs::rcp), the
+// quotient n/e (n = k or e - k, whole numbers) is formed as q0 = n * r,
+// corrected once by the exact fp32 remainder n - q0 * e (one fused
 // multiply-add), q = q0 + rem * r (another).  For every 0 <= k < e <= 4096
-// this gives exactly fp32(k/e) and fp32(1 - k/e) rounded from float64 (checked
-// on all 8,390,656 pairs on the host); kMaxBlend keeps e within that range.
-__device__ __forceinline__ float recip_of(int e) { return (float)(1.0 / (double)e); }
+// this gives exactly the float64-rounded weights (checked on all 8,390,656
+// pairs on the host); kMaxBlend keeps e within that range.
 
 __device__ __forceinline__ float quotient(float n, float e, float r) {
   const float q0 = n * r;
@@ -132,7 +128,7 @@ __device__ __forceinline__ float quotient(float n, float e, float r) {
   return fmaf(rem, r, q0);
 }
 
-// (w_a, w_b) of position k of a seam of extent e, r = recip_of(e)
+// (w_a, w_b) of position k of a seam of extent e, r = fp32(1/e)
 __device__ __forceinline__ float2 coefficients_r(int k, int e, float r) {
   return make_float2(quotient((float)(e - k), (float)e, r), quotient((float)k, (float)e, r));
 }
@@ -695,7 +691,8 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) void blend_span_kernel(const Blen
   constexpr int EB = Elem<DT>::bytes;
   // LDS: [span_w] column coefficients, [rows_per_block] row coefficients, [span_k] SpanCol
   extern __shared__ float2 s_tab[];
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x;
+  constexpr int nthr = SB_BLEND_THREADS; // a constant: no implicit-argument load
   const int nw = A.n_w, nh = A.n_h, nt = A.n_t;
 
   // ---- span: tile columns [ja, jb) ----
@@ -730,7 +727,7 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) void blend_span_kernel(const Blen
     const int j = min((int)fdiv((uint32_t)x, A.div_Rw), nw - 1);
     const int xl = x - j * A.R[2];
     const int ew = j > 0 ? min(A.E[2], min(A.ext[2][j - 1], A.ext[2][j])) : 0;
-    if (xl < ew) s_cw[x - xs0] = coefficients(xl, ew);
+    if (xl < ew) s_cw[x - xs0] = coefficients_r(xl, ew, A.rcp[2][j]);
   }
   // row coefficients of the band's rows that lie in a row seam
   if (A.E[1] > 0)
@@ -739,9 +736,9 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) void blend_span_kernel(const Blen
       const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
       const int y = yo - i * A.R[1];
       const int eh = i > 0 ? min(A.E[1], min(A.ext[1][i - 1], A.ext[1][i])) : 0;
-      if (y < eh) s_ch[k] = coefficients(y, eh);
+      if (y < eh) s_ch[k] = coefficients_r(y, eh, A.rcp[1][i]);
     }
-  const float2 ct = ts ? coefficients(f, et) : make_float2(0.f, 0.f);
+  const float2 ct = ts ? coefficients_r(f, et, A.rcp[0][tau]) : make_float2(0.f, 0.f);
 
   const char *const *P = (const char *const *)A.ptr;
   auto tile = [&](int tq, int ti, int tj) {
