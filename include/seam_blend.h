@@ -97,6 +97,10 @@ int vae_tile_blend_stitch_output_extents(const int64_t grid[6], const int64_t *t
  * already blended) along frames and cropped.  Bit-exact for every dtype.
  * Each output element is written exactly once; no scratch memory.
  * N*C == 0 is a no-op that accepts null tile and output pointers.
+ * Limits (SB_EGEOM beyond them, before any launch): clamped blend extents up
+ * to 4096; when every W seam and crop is narrower than 16 vectors (the
+ * narrow-seam layout) a launch window of more than 2^24 - 1 output frames is
+ * refused; otherwise any frame count is taken, in several launches.
  */
 int vae_tile_blend_stitch(const void *const *tiles, const int64_t grid[6],
                           const int64_t *tile_extents, const int64_t blend_extent[3],

@@ -353,6 +353,9 @@ typedef __attribute__((address_space(1))) char *GOut;
 struct PtrPair {
   const char *a, *b; // pointer-table entries k-1 and k
 };
+// the pair of entry 0 starts at the output pointer, the argument word before
+// the table: read with it, never used
+static_assert(offsetof(BlendArgs, ptr) == sizeof(void *), "the table follows the output pointer");
 
 // The tiles the closed form reads for one tile row of a segment: (i,j),
 // (i-1,j), (i,j-1), (i-1,j-1) of chunk tau, then the same in chunk tau-1.
