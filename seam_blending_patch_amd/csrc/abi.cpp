@@ -596,10 +596,6 @@ int groupnorm_call(const void *x, int ndim, const int64_t *shape, int64_t groups
   a.part = (float *)workspace;
   a.patch_stats = patch_stats;
   a.eps = eps;
-  // Pass-2 load order: x first when the grid is at most 16 blocks per CU
-  // (the video activation, 5 per CU, and the 256x256 one, 16: 5% and 1%
-  // faster), the small loads first above that (the 512x512 one, 64 per CU: 2%)
-  a.x_first = (int64_t)a.N * a.C * a.chunks2 <= 16 * (int64_t)cu_count() ? 1 : 0;
   hipError_t e = sb_launch_groupnorm(a, dtype, vec16 ? 1 : 0, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SB_ELAUNCH, "groupnorm launch failed: %s", hipGetErrorString(e));
   return SB_OK;

@@ -107,7 +107,6 @@ struct GNArgs {
   int64_t per2;       // vectors per pass-2 block
   FastDiv div_C, div_Cg; // plane -> (n, c) and channel -> group
   FastDiv div_P, div_G;  // pass-1 block -> (n, group, patch)
-  int32_t x_first;    // pass 2 requests x before the partials (small grids)
   int32_t rows_layout; // pass 1 reads whole rows (patches cut the innermost axis)
   uint32_t plane0;    // first (n, c) plane of this pass-2 launch
 };
