@@ -124,6 +124,13 @@ def test_traffic_record_from_counter_runs(tmp_path):
         if name.startswith("config4"):
             for f, h in r["sources_sha256"].items():
                 assert os.path.exists(os.path.join(ROOT, f)) and len(h) == 64
+    # the readable table: one row per launch with the scaled bytes and the excess
+    rec["launches"].pop("ramp:other")
+    json.dump(rec, open(out, "w"))
+    md = traffic.traffic_table(str(out))
+    assert md.count("| config4-") == 3
+    assert f"| {blend['hbm_bytes_per_launch']:.0f} | {blend['algorithmic_bytes_per_launch']} |" in md
+    assert "--pmc FETCH_SIZE" in md and "benchkit.traffic traffic <w>" in md
 
 
 def test_kernel_trace_summary(tmp_path):
