@@ -55,6 +55,17 @@ def test_config_full_size_bitexact(sb, cfg):
     compare.assert_bitexact(from_dev(out, w.dtype), want, w.dtype, f"config {cfg} poisoned out")
 
 
+@pytest.mark.parametrize("cfg,dtype", [(2, "bf16"), (2, "fp32"), (3, "fp16"), (3, "fp32"), (4, "fp16"),
+                                       (4, "fp32"), (5, "bf16")])
+def test_config_geometries_in_other_dtypes(sb, cfg, dtype):
+    # every workload's tile geometry at full size in the dtypes it is not
+    # specified in: the same launch layout (segment widths, bands, windows)
+    # with 2- or 4-byte elements, bit-exact against the oracle
+    base = workloads.CONFIGS[cfg].blend
+    w = dataclasses.replace(base, name=f"{base.name}-as-{dtype}", dtype=dtype, seed=40 + cfg)
+    check(sb, w, workloads.draw_tiles(w), f"config {cfg} geometry")
+
+
 @pytest.mark.parametrize("name", sorted(workloads.ENCODE_BLEND_WORKLOADS))
 def test_stock_tiled_encode_latents_bitexact(sb, name):
     # the same blend on encoder outputs: 4-channel latent tiles of 64 with a
