@@ -5,6 +5,8 @@ oracle (unsplit GroupNorm), within the stated tolerances read as
 plus the per-patch statistics against the oracle's double per-patch ones."""
 from __future__ import annotations
 
+import dataclasses
+
 import sys
 
 import numpy as np
@@ -66,6 +68,16 @@ def test_config_full_size(sb, cfg):
     check(sb, gw, x, g, b, f"config {cfg}")
 
 
+@pytest.mark.parametrize("cfg,dtype", [(3, "fp16"), (3, "fp32"), (4, "fp16"), (4, "fp32")])
+def test_config_shapes_in_other_dtypes(sb, cfg, dtype):
+    # the workloads' activation shapes, patch splits and offsets at full size
+    # in dtypes they are not specified in, at that dtype's tolerance
+    base = workloads.CONFIGS[cfg].groupnorm
+    gw = dataclasses.replace(base, name=f"{base.name}-as-{dtype}", dtype=dtype, seed=60 + cfg)
+    x, g, b = workloads.draw_groupnorm(gw)
+    check(sb, gw, x, g, b, f"config {cfg} shape")
+
+
 def _gw(shape, dtype, G, axis, P, seed, affine=True, offset=("uniform", -2.0, 2.0)):
     return workloads.GroupNormWorkload("rand", dtype, shape, G, axis, P, 1e-6, seed, offset=offset,
                                        affine=affine)
@@ -82,7 +94,7 @@ CASES = [
     ((1, 8, 64, 64), 2, 3, 64),      # the maximum patch count
     ((2, 4, 100), 2, 2, 3),          # 3-D
     ((1, 64, 40, 40), 32, 2, 1),     # a single patch
-    ((1, 8192, 16, 16), 64, 2, 3),   # 8192 normalise blocks: the large-grid load order
+    ((1, 8192, 16, 16), 64, 2, 3),   # 8192 (n, c) planes of one normalise block each
     ((1, 8, 6, 5), 2, 3, 9),         # W split, more patches than columns: empty patches
     ((1, 4, 3, 4096), 2, 3, 4),      # W split, rows of 512-1024 vectors
     ((1, 4, 3, 8192), 2, 3, 3),      # W split, ragged, rows wider than one block: patch-run path
