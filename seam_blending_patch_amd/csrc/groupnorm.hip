@@ -22,10 +22,11 @@
 //   running (count, m, M2) with Chan's pairwise formula
 //       d = mu_B - mu_A, n = n_A + n_B, mu = mu_A + d n_B / n,
 //       M2 = M2_A + M2_B + d^2 n_A n_B / n
-//   (Welford's update, a batch at a time).  The block merges its threads the
-//   same way, first across the wavefront with shuffles, then across the 4
-//   waves in LDS, and writes one partial (count, m, M2, K_g) to the workspace;
-//   counts are integers.
+//   (Welford's update, a batch at a time).  The block merges its threads by
+//   the many-set form of the same merge, n = sum n_l, mu = sum n_l mu_l / n,
+//   M2 = sum (M2_l + n_l (mu_l - mu)^2), first across the wavefront (sums by
+//   DPP shifts), then across its waves through LDS, and writes one partial
+//   (count, m, M2, K_g) to the workspace; counts are integers.
 // Pass 2 (gn_norm_kernel): one block per (n, c) plane chunk.  Every wave
 //   requests the P x CPP partials of its group, gamma, beta and its vectors
 //   of x, and merges the partials with a fixed shuffle tree (chunks of a patch
@@ -104,17 +105,42 @@ __device__ __forceinline__ Stat readlane_stat(const Stat &s, int l) {
               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s.m2), l))};
 }
 
-// The whole wavefront's statistics by the fixed tree lane l += lane l + o for
-// o = 1, 2, 4, 8 (DPP, inside rows of 16), then rows 0+1, 2+3 and the two
-// halves (read lanes 0, 16, 32, 48).  Returned in every lane.
-__device__ __forceinline__ Stat wave_merge(Stat st, int lane) {
-  tree_level<1>(st, lane);
-  tree_level<2>(st, lane);
-  tree_level<4>(st, lane);
-  tree_level<8>(st, lane);
-  const Stat lo = chan_merge(readlane_stat(st, 0), readlane_stat(st, 16));
-  const Stat hi = chan_merge(readlane_stat(st, 32), readlane_stat(st, 48));
-  return chan_merge(lo, hi);
+// Sum over the wavefront by a fixed tree: DPP row shifts by 1, 2, 4 and 8
+// (lane l adds lane l + o of its row of 16), then the four row leaders (lanes
+// 0, 16, 32, 48) read as scalars and added in pairs.  Returned in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x102, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x108, 0xf, 0xf, false));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x101, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x102, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x108, 0xf, 0xf, false);
+  return ((uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16)) +
+         ((uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+}
+
+// The whole wavefront's statistics from the merge of many sets at once:
+// n = sum n_l, mean = sum n_l mean_l / n, M2 = sum (M2_l + n_l (mean_l -
+// mean)^2) -- two rounds of plain sums (the second needs the merged mean)
+// instead of a chain of pairwise merges, and every term of the M2 sum is
+// non-negative.  Lanes without values (n_l = 0) add nothing.  Returned in
+// every lane.
+__device__ __forceinline__ Stat wave_merge(const Stat &st) {
+  const float nl = (float)st.n;
+  const uint32_t n = wave_sum(st.n);
+  if (n == 0) return Stat{0u, 0.f, 0.f};
+  const float mean = wave_sum(nl * st.mean) * __builtin_amdgcn_rcpf((float)n);
+  const float d = st.mean - mean;
+  return Stat{n, mean, wave_sum(fmaf(nl * d, d, st.m2))};
 }
 
 #ifndef SB_GN_STATS_BATCH
@@ -253,16 +279,28 @@ __global__ __launch_bounds__(kStatsThreads) void gn_stats_kernel(const GNArgs A,
     load_batch(base);
     accumulate_batch<DT, VB>(st, v, ok, K);
   }
-  const int lane = tid & 63;
-  st = wave_merge(st, lane);
+  st = wave_merge(st);
   __shared__ Stat s_w[kStatsWaves];
-  if (lane == 0) s_w[tid >> 6] = st;
+  if ((tid & 63) == 0) s_w[tid >> 6] = st;
   __syncthreads();
   if (tid == 0) {
-    Stat m = s_w[0];
-    for (int w = 1; w < kStatsWaves; ++w) m = chan_merge(m, s_w[w]);
+    // the waves merged the same way as the lanes
+    uint32_t n = 0;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStatsWaves; ++w) {
+      n += s_w[w].n;
+      s = fmaf((float)s_w[w].n, s_w[w].mean, s);
+    }
+    const float mean = n > 0 ? s * __builtin_amdgcn_rcpf((float)n) : 0.f;
+    float m2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStatsWaves; ++w) {
+      const float d = s_w[w].mean - mean;
+      m2 += fmaf((float)s_w[w].n * d, d, s_w[w].m2);
+    }
     float4 *dst = reinterpret_cast<float4 *>(A.part) + b;
-    *dst = make_float4(__uint_as_float(m.n), m.mean, m.m2, K);
+    *dst = make_float4(__uint_as_float(n), mean, m2, K);
   }
 }
 
@@ -418,7 +456,7 @@ __global__ __launch_bounds__(kNormThreads) void gn_norm_kernel(const GNArgs A) {
   const float gam = A.gamma ? widen<DT>(graw) : 1.0f;
   const float bet = A.beta ? widen<DT>(braw) : 0.0f;
 
-  // merge the group's partials with the fixed tree of wave_merge
+  // merge the group's partials with a fixed tree of pairwise merges
   Stat st{__float_as_uint(src.x), src.y, src.z};
   // the group shift K_g (the same in every partial of the group; lane 0 holds partial 0)
   const float Kg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src.w), 0));
@@ -428,8 +466,9 @@ __global__ __launch_bounds__(kNormThreads) void gn_norm_kernel(const GNArgs A) {
     float *d = A.patch_stats + ((size_t)ng * A.P + lane) * 3;
     d[0] = (float)st.n; d[1] = st.n > 0 ? Kg + st.mean : 0.f; d[2] = st.m2;
   }
-  // the fixed tree of wave_merge; after the level at which 2o == CPP, lane
-  // p * CPP holds patch p, which the writer records
+  // pairwise merges at levels o = 1, 2, 4, 8 inside rows (DPP), then rows 0+1,
+  // 2+3 and the two halves; after the level at which 2o == CPP, lane p * CPP
+  // holds patch p, which the writer records
   auto record = [&](const Stat &v, int p) {
     float *d = A.patch_stats + ((size_t)ng * A.P + p) * 3;
     d[0] = (float)v.n; d[1] = v.n > 0 ? Kg + v.mean : 0.f; d[2] = v.m2;
