@@ -29,12 +29,13 @@
 //   (count, m, M2, K_g) to the workspace; counts are integers.
 // Pass 2 (gn_norm_kernel): one block per (n, c) plane chunk.  Every wave
 //   requests the P x CPP partials of its group, gamma, beta and its vectors
-//   of x, and merges the partials with a fixed shuffle tree (chunks of a patch
-//   first, then patches) -- the same order in every block, so results are
-//   deterministic -- and streams y = ((x - K_g) - m) * (rstd * gamma_c) +
-//   beta_c back out with nontemporal stores.  K_g comes from the workspace,
-//   not from x, so out may alias x.  Wave 0 of the first block of each group
-//   writes the optional per-patch statistics.
+//   of x, and merges the partials by the same many-set formula over fixed
+//   sum trees -- the same order in every block, so results are deterministic
+//   -- and streams y = ((x - K_g) - m) * (rstd * gamma_c) + beta_c back out
+//   with nontemporal stores.  K_g comes from the workspace, not from x, so
+//   out may alias x.  Wave 0 of the first block of each group writes the
+//   optional per-patch statistics, from a tree of pairwise merges (chunks of
+//   a patch first, then patches).
 
 #include "sb_internal.h"
 #include "sb_vec.h"
@@ -456,43 +457,43 @@ __global__ __launch_bounds__(kNormThreads) void gn_norm_kernel(const GNArgs A) {
   const float gam = A.gamma ? widen<DT>(graw) : 1.0f;
   const float bet = A.beta ? widen<DT>(braw) : 0.0f;
 
-  // merge the group's partials with a fixed tree of pairwise merges
+  // the group's statistics from its partials (lane l holds partial l)
   Stat st{__float_as_uint(src.x), src.y, src.z};
   // the group shift K_g (the same in every partial of the group; lane 0 holds partial 0)
   const float Kg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src.w), 0));
   const bool writer = A.patch_stats != nullptr && chunk == 0 && ch == g * A.Cg && tid < 64;
   const int cppl = A.CPP; // lanes per patch
-  if (writer && cppl == 1 && lane < A.P) {
-    float *d = A.patch_stats + ((size_t)ng * A.P + lane) * 3;
-    d[0] = (float)st.n; d[1] = st.n > 0 ? Kg + st.mean : 0.f; d[2] = st.m2;
+  if (writer) {
+    // the writer wave also runs a tree of pairwise merges, levels o = 1, 2,
+    // 4, 8 inside rows (DPP), then rows 0+1, 2+3 and the two halves, whose
+    // levels hold each patch's statistics on the way: after the level at
+    // which 2o == CPP, lane p * CPP holds patch p
+    Stat t = st;
+    auto record = [&](const Stat &v, int p) {
+      float *d = A.patch_stats + ((size_t)ng * A.P + p) * 3;
+      d[0] = (float)v.n; d[1] = v.n > 0 ? Kg + v.mean : 0.f; d[2] = v.m2;
+    };
+    auto record_rows = [&](int o) {
+      if (2 * o == cppl && (lane & (cppl - 1)) == 0 && (lane >> A.log2CPP) < A.P) record(t, lane >> A.log2CPP);
+    };
+    if (cppl == 1 && lane < A.P) record(t, lane);
+    tree_level<1>(t, lane);
+    record_rows(1);
+    tree_level<2>(t, lane);
+    record_rows(2);
+    tree_level<4>(t, lane);
+    record_rows(4);
+    tree_level<8>(t, lane);
+    record_rows(8);
+    const Stat lo = chan_merge(readlane_stat(t, 0), readlane_stat(t, 16));
+    const Stat hi = chan_merge(readlane_stat(t, 32), readlane_stat(t, 48));
+    if (cppl == 32 && lane == 0) {
+      record(lo, 0);
+      if (A.P > 1) record(hi, 1);
+    }
+    if (cppl == 64 && lane == 0) record(chan_merge(lo, hi), 0);
   }
-  // pairwise merges at levels o = 1, 2, 4, 8 inside rows (DPP), then rows 0+1,
-  // 2+3 and the two halves; after the level at which 2o == CPP, lane p * CPP
-  // holds patch p, which the writer records
-  auto record = [&](const Stat &v, int p) {
-    float *d = A.patch_stats + ((size_t)ng * A.P + p) * 3;
-    d[0] = (float)v.n; d[1] = v.n > 0 ? Kg + v.mean : 0.f; d[2] = v.m2;
-  };
-  auto record_rows = [&](int o) {
-    if (writer && 2 * o == cppl && (lane & (cppl - 1)) == 0 && (lane >> A.log2CPP) < A.P)
-      record(st, lane >> A.log2CPP);
-  };
-  tree_level<1>(st, lane);
-  record_rows(1);
-  tree_level<2>(st, lane);
-  record_rows(2);
-  tree_level<4>(st, lane);
-  record_rows(4);
-  tree_level<8>(st, lane);
-  record_rows(8);
-  const Stat lo = chan_merge(readlane_stat(st, 0), readlane_stat(st, 16));
-  const Stat hi = chan_merge(readlane_stat(st, 32), readlane_stat(st, 48));
-  if (writer && cppl == 32 && lane == 0) {
-    record(lo, 0);
-    if (A.P > 1) record(hi, 1);
-  }
-  st = chan_merge(lo, hi);
-  if (writer && cppl == 64 && lane == 0) record(st, 0);
+  st = wave_merge(st);
   const float cnt = (float)st.n;
   const float mean = st.mean;
   const float m2 = st.m2;
