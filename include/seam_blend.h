@@ -134,8 +134,10 @@ size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape, int64_t g
  *                (0, 0, 0) for an empty patch.
  *   stream       hipStream_t or NULL.
  * Result: per (n, g), mean and M2 over the C/G channels and all spatial
- * positions, obtained by Chan-merging fp32 partial statistics in a fixed order
- * (chunks of a patch, then patches); var = M2 / count; rstd = 1/sqrt(var+eps);
+ * positions, obtained by merging fp32 partial statistics in a fixed order:
+ * count, mean = sum n_k mean_k / count, M2 = sum (M2_k + n_k (mean_k -
+ * mean)^2) over the partials (Chan's merge taken over many sets at once);
+ * var = M2 / count; rstd = 1/sqrt(var+eps);
  * y = (x - mean) * rstd * gamma_c + beta_c in fp32, rounded once to dtype.
  * Each thread folds its values into (count, mean, M2) a batch at a time: the
  * batch's mean and squared deviations by two passes, then a Chan merge

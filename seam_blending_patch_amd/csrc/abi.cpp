@@ -202,7 +202,6 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
 
   sb::BlendArgs A;
   std::memset(&A, 0, sizeof A);
-  int64_t ew_max = 0;
   for (int a = 0; a < 3; ++a) {
     const Axis &X = G.ax[a];
     for (int64_t k = 0; k < X.n; ++k) {
@@ -212,7 +211,6 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
       // the seam's reciprocal, rounded once from float64 as the kernel's
       // coefficient formula requires
       A.rcp[a][k] = X.e[k] > 0 ? (float)(1.0 / (double)X.e[k]) : 0.f;
-      if (a == 2) ew_max = std::max(ew_max, X.e[k]);
     }
   }
   A.out = out;
@@ -224,7 +222,6 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   A.LT = (int32_t)At.L; A.LH = (int32_t)Ah.L; A.LW = (int32_t)Aw.L;
   A.div_Rt = sb::make_fastdiv((uint32_t)At.R);
   A.div_Rh = sb::make_fastdiv((uint32_t)Ah.R);
-  A.ew_max = (int32_t)ew_max;
   {
     // 32-bit lane offsets when every (plane, frame) slice of a tile and every
     // band of output rows as tall as a tile stays below 2^31 bytes
@@ -247,7 +244,7 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
     A.nt_store = traffic < (double)(128 << 20) ? 1 : 0;
   }
   // Rows per block.  Each block pays a fixed start-up (argument loads; in the
-  // span layout also its coefficient tables and a barrier), so blocks are made
+  // span layout also its column records and a barrier), so blocks are made
   // as large as the problem allows while still giving every CU several blocks: about
   // total / (cus * SB_BLEND_BLOCKS_PER_CU) vectors in the widest W segment,
   // clamped to [1024, 8192]; the band height is then aligned to the row seams
@@ -331,15 +328,10 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   rows_pb = std::max<int64_t>(rows_pb, (Ah.L + sb::kMaxBlocksYZ - 1) / sb::kMaxBlocksYZ);
   A.rows_per_block = (int32_t)rows_pb;
   A.span_k = (int32_t)span_k;
-  A.span_w = (int32_t)span_w;
   A.div_Rw = sb::make_fastdiv((uint32_t)Aw.R);
-  // dynamic LDS: the span layout's coefficient tables and column table (the
-  // segment layout forms its coefficients in registers and needs none)
-  const size_t lds = span ? (size_t)(span_w + rows_pb) * sizeof(float2) + (size_t)span_k * sizeof(sb::SpanCol)
-                          : 0;
-  if (lds > 65536)
-    return fail(SB_EGEOM, "output of %lld rows needs %zu bytes of LDS per block in the narrow-seam layout",
-                (long long)Ah.L, lds);
+  // dynamic LDS: the span layout's column records (both layouts form their
+  // seam coefficients in registers)
+  const size_t lds = span ? (size_t)span_k * sizeof(sb::SpanCol) : 0;
   hipStream_t st = (hipStream_t)stream;
   const int64_t n_wseg = span ? n_spans : 2 * Aw.n - 1;
 

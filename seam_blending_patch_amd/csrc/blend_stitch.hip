@@ -347,7 +347,6 @@ __device__ __forceinline__ void run_rows(const Run &R, int tid, int nthreads) {
   }
 }
 
-typedef const __attribute__((address_space(1))) char *GPtr;
 typedef __attribute__((address_space(1))) char *GOut;
 
 struct PtrPair {
@@ -575,59 +574,64 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_ke
 // frame classes stay block-uniform per run.  Same closed form, same
 // arithmetic, element by element through fp32.
 // ---------------------------------------------------------------------------
+#ifndef SB_SPAN_U
+#define SB_SPAN_U 2
+#endif
 struct SpanRun {
   char *o;                       // output at (local row 0, first column of the span)
   int64_t opitch;
   int y0, y1;                    // local rows of the tile row
   int xs0, wv, ja, nw;           // first output column, vectors per row, first tile column, n_w
-  float inv_wv;
-  FastDiv div_Rw;
-  const float2 *ch, *cw;         // row coefficients by local row; column coefficients by span column
-  float2 ct;
+  uint32_t Rwm, Rws;             // division by the column row limit R_w (magic multiplier, shift)
+  int eh;                        // row seam extent of the run's tile row (row seams)
+  float rh;                      // fp32(1/eh)
+  float2 ct;                     // frame coefficient (frame seams)
 };
 
 template <int DT, int VB, bool HS, bool TS>
 __device__ __forceinline__ void span_rows(const SpanRun &R, const SpanCol *cols, int tid, int nthreads) {
   constexpr int V = VecInfo<DT, VB>::V;
   constexpr int EB = Elem<DT>::bytes;
-  constexpr int U = 2; // output vectors per thread per batch
+  constexpr int U = SB_SPAN_U; // output vectors per thread per batch
   const int nvec = (R.y1 - R.y0) * R.wv;
+  const float rwv = __builtin_amdgcn_rcpf((float)R.wv);
   for (int q0 = tid; q0 < nvec; q0 += nthreads * U) {
     Vec<VB> m[U], up[U], lf[U], cn[U], pm[U], pu[U], pl[U], pc[U];
-    int yy[U], xs[U];
+    int yy[U], xs[U], xl[U], ew[U];
+    float rw[U];
     bool ok[U], ws[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int q = q0 + k * nthreads;
       ok[k] = q < nvec;
-      int r = (int)((float)q * R.inv_wv);
-      r -= (r * R.wv > q) ? 1 : 0;
-      r += ((r + 1) * R.wv <= q) ? 1 : 0;
-      const int y = R.y0 + r;
-      const int xo = (q - r * R.wv) * V;             // column within the span
+      const int2 rq = divmod_small(q, R.wv, rwv);
+      const int y = R.y0 + rq.x;
+      const int xo = rq.y * V;                       // column within the span
       const int x = R.xs0 + xo;                      // output column
-      const int j = min((int)fdiv((uint32_t)x, R.div_Rw), R.nw - 1);
+      const int j = min((int)fdiv_ms((uint32_t)x, R.Rwm, R.Rws), R.nw - 1);
       yy[k] = y;
       xs[k] = xo;
       ws[k] = false;
       if (ok[k]) {
         const SpanCol &C = cols[j - R.ja];
-        const int xl = x - C.xbase;                  // column within tile j
-        ws[k] = xl < C.ews;
-        const int64_t oj = (int64_t)y * C.pitch_j + (int64_t)xl * EB;
-        const int64_t op = (int64_t)y * C.pitch_p + (int64_t)xl * EB;
-        m[k] = vload<VB, SB_BLEND_NT>(C.m + oj);
-        if constexpr (HS) up[k] = vload<VB, SB_BLEND_NT>(C.u + oj);
+        xl[k] = x - C.xbase;                         // column within tile j
+        ws[k] = xl[k] < C.ews;
+        ew[k] = C.ew;
+        rw[k] = C.rw;
+        const int64_t oj = (int64_t)y * C.pitch_j + (int64_t)xl[k] * EB;
+        const int64_t op = (int64_t)y * C.pitch_p + (int64_t)xl[k] * EB;
+        m[k] = vload<VB, SB_BLEND_NT>((const char *)(C.m + oj));
+        if constexpr (HS) up[k] = vload<VB, SB_BLEND_NT>((const char *)(C.u + oj));
         if (ws[k]) {
-          lf[k] = vload<VB, SB_BLEND_NT>(C.l + op);
-          if constexpr (HS) cn[k] = vload<VB, SB_BLEND_NT>(C.c + op);
+          lf[k] = vload<VB, SB_BLEND_NT>((const char *)(C.l + op));
+          if constexpr (HS) cn[k] = vload<VB, SB_BLEND_NT>((const char *)(C.c + op));
         }
         if constexpr (TS) {
-          pm[k] = vload<VB, SB_BLEND_NT>(C.pm + oj);
-          if constexpr (HS) pu[k] = vload<VB, SB_BLEND_NT>(C.pu + oj);
+          pm[k] = vload<VB, SB_BLEND_NT>((const char *)(C.pm + oj));
+          if constexpr (HS) pu[k] = vload<VB, SB_BLEND_NT>((const char *)(C.pu + oj));
           if (ws[k]) {
-            pl[k] = vload<VB, SB_BLEND_NT>(C.pl + op);
-            if constexpr (HS) pc[k] = vload<VB, SB_BLEND_NT>(C.pc + op);
+            pl[k] = vload<VB, SB_BLEND_NT>((const char *)(C.pl + op));
+            if constexpr (HS) pc[k] = vload<VB, SB_BLEND_NT>((const char *)(C.pc + op));
           }
         }
       }
@@ -640,12 +644,66 @@ __device__ __forceinline__ void span_rows(const SpanRun &R, const SpanCol *cols,
         vstore<VB, false>(dst, m[k]);
         continue;
       }
+      if constexpr (DT != DT_F32 && VB == 16) {
+        // packed pairs of 16-bit elements, as in run_rows
+        constexpr int NW = Vec<VB>::NW;
+        const bool w = ws[k];
+        f32x2 ha, hb;
+        if constexpr (HS) {
+          const float2 c = coefficients_r(yy[k], R.eh, R.rh);
+          ha.x = ha.y = c.x;
+          hb.x = hb.y = c.y;
+        }
+        f32x2 wa[NW], wb[NW];
+        if (w) {
+#pragma unroll
+          for (int e = 0; e < NW; ++e) {
+            const float2 c0 = coefficients_r(xl[k] + 2 * e, ew[k], rw[k]);
+            const float2 c1 = coefficients_r(xl[k] + 2 * e + 1, ew[k], rw[k]);
+            wa[e].x = c0.x; wa[e].y = c1.x;
+            wb[e].x = c0.y; wb[e].y = c1.y;
+          }
+        }
+        auto spatial2 = [&](const Vec<VB> &vm, const Vec<VB> &vu, const Vec<VB> &vl, const Vec<VB> &vc,
+                            Vec<VB> &o) {
+          o = vm;
+#pragma unroll
+          for (int e = 0; e < NW; ++e) {
+            uint32_t sv = vm.w[e];
+            if constexpr (HS) {
+              uint32_t Uw = vu.w[e];
+              if (w) Uw = crossfade2<DT>(vc.w[e], Uw, wa[e], wb[e]);
+              sv = crossfade2<DT>(Uw, sv, ha, hb);
+            }
+            if (w) {
+              uint32_t Lw = vl.w[e];
+              if constexpr (HS) Lw = crossfade2<DT>(vc.w[e], Lw, ha, hb);
+              sv = crossfade2<DT>(Lw, sv, wa[e], wb[e]);
+            }
+            o.w[e] = sv;
+          }
+        };
+        Vec<VB> S;
+        spatial2(m[k], up[k], lf[k], cn[k], S);
+        if constexpr (TS) {
+          Vec<VB> Sp;
+          spatial2(pm[k], pu[k], pl[k], pc[k], Sp);
+          f32x2 ta, tb;
+          ta.x = ta.y = R.ct.x;
+          tb.x = tb.y = R.ct.y;
+#pragma unroll
+          for (int e = 0; e < NW; ++e) S.w[e] = crossfade2<DT>(Sp.w[e], S.w[e], ta, tb);
+        }
+        vstore<VB, false>(dst, S);
+        continue;
+      }
+      // seam coefficients formed in registers, as in the segment layout
       float2 chh = make_float2(0.f, 0.f);
-      if constexpr (HS) chh = R.ch[yy[k]];
+      if constexpr (HS) chh = coefficients_r(yy[k], R.eh, R.rh);
       float2 cww[V];
       if (ws[k]) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) cww[e] = R.cw[xs[k] + e];
+        for (int e = 0; e < V; ++e) cww[e] = coefficients_r(xl[k] + e, ew[k], rw[k]);
       }
       const bool w = ws[k];
       auto spatial = [&](const Vec<VB> &vm, const Vec<VB> &vu, const Vec<VB> &vl, const Vec<VB> &vc,
@@ -692,119 +750,165 @@ __device__ __forceinline__ void span_rows(const SpanRun &R, const SpanCol *cols,
 template <int DT, int VB>
 __global__ __launch_bounds__(SB_BLEND_THREADS) void blend_span_kernel(const BlendArgs A) {
   constexpr int EB = Elem<DT>::bytes;
-  // LDS: [span_w] column coefficients, [rows_per_block] row coefficients, [span_k] SpanCol
-  extern __shared__ float2 s_tab[];
+  extern __shared__ float2 s_tab[]; // [span_k] SpanCol
+  SpanCol *s_col = reinterpret_cast<SpanCol *>(s_tab);
   const int tid = threadIdx.x;
   constexpr int nthr = SB_BLEND_THREADS; // a constant: no implicit-argument load
-  const int nw = A.n_w, nh = A.n_h, nt = A.n_t;
+
+  // Every launch argument the block decode reads, read at entry and pinned in
+  // scalar registers (one round of scalar loads), as in blend_stitch_kernel.
+  int32_t nw = A.n_w, nh = A.n_h, nt = A.n_t, E0 = A.E[0], E1 = A.E[1], E2 = A.E[2];
+  int32_t R0 = A.R[0], R1 = A.R[1], R2 = A.R[2], LT = A.LT, LH = A.LH, LW = A.LW;
+  int32_t taub = A.taub, ib = A.ib, ptr_nh = A.ptr_nh, F0 = A.F0, nF = A.nF, Y0 = A.Y0, nY = A.nY;
+  int32_t plane0 = A.plane0, rows_pb = A.rows_per_block, span_k = A.span_k;
+  uint32_t nFm = A.div_nF.m, nFs = A.div_nF.s, Rtm = A.div_Rt.m, Rts = A.div_Rt.s;
+  uint32_t Rhm = A.div_Rh.m, Rhs = A.div_Rh.s, Rwm = A.div_Rw.m, Rws = A.div_Rw.s;
+  GOut outp = (GOut)A.out;
+  asm volatile("" : "+s"(nw), "+s"(nh), "+s"(nt), "+s"(E0), "+s"(E1), "+s"(E2), "+s"(R0), "+s"(R1), "+s"(R2),
+               "+s"(LT), "+s"(LH), "+s"(LW), "+s"(taub), "+s"(ib), "+s"(ptr_nh), "+s"(F0));
+  asm volatile("" : "+s"(nF), "+s"(Y0), "+s"(nY), "+s"(plane0), "+s"(rows_pb), "+s"(span_k), "+s"(nFm),
+               "+s"(nFs), "+s"(Rtm), "+s"(Rts), "+s"(Rhm), "+s"(Rhs), "+s"(Rwm), "+s"(Rws), "+s"(outp));
 
   // ---- span: tile columns [ja, jb) ----
-  const int ja = blockIdx.y * A.span_k;
-  const int jb = min(ja + A.span_k, nw);
-  const int xs0 = ja * A.R[2];
-  const int xs1 = jb == nw ? A.LW : jb * A.R[2];
+  const int ja = (int)blockIdx.y * span_k;
+  const int jb = min(ja + span_k, nw);
+  const int xs0 = ja * R2;
+  const int xs1 = jb == nw ? LW : jb * R2;
 
   // ---- frame (block-uniform), as in blend_stitch_kernel ----
   const uint32_t pz = blockIdx.x;
-  const uint32_t pli = fdiv(pz, A.div_nF);
-  const int64_t plane = (int64_t)A.plane0 + pli;
-  const int f_out = A.F0 + (int)(pz - pli * (uint32_t)A.nF);
-  const int tau = min((int)fdiv((uint32_t)f_out, A.div_Rt), nt - 1);
-  const int f = f_out - tau * A.R[0];
-  const int tt = A.ext[0][tau];
-  const int tp = tau > 0 ? A.ext[0][tau - 1] : 0;
-  const int et = tau > 0 ? min(A.E[0], min(tp, tt)) : 0;
-  const bool ts = f < et;
-  const int fp = tp - et + f;
+  const uint32_t pli = fdiv_ms(pz, nFm, nFs);
+  const uint32_t plane = (uint32_t)plane0 + pli; // N * C < 2^31
+  const int f_out = F0 + (int)(pz - pli * (uint32_t)nF);
+  const int tau = min((int)fdiv_ms((uint32_t)f_out, Rtm, Rts), nt - 1);
+  const int f = f_out - tau * R0;
+  const int r0 = (int)blockIdx.z * rows_pb;
+  const int r1 = min(r0 + rows_pb, nY);
+  const int yo0 = Y0 + r0, yo1 = Y0 + r1;
+  const int ia = min((int)fdiv_ms((uint32_t)yo0, Rhm, Rhs), nh - 1); // first run's tile row
 
-  const int r0 = blockIdx.z * A.rows_per_block;
-  const int r1 = min(r0 + A.rows_per_block, A.nY);
-  const int yo0 = A.Y0 + r0, yo1 = A.Y0 + r1;
+  // tile-pointer table: entry b's pair (entries b-1, b), as in blend_stitch_kernel
+  const char *const tab = (const char *)A.ptr - sizeof(void *);
+  auto pair = [&](uint32_t b) { return *(const PtrPair *)(tab + (size_t)(b * (uint32_t)sizeof(void *))); };
 
-  float2 *s_cw = s_tab;
-  float2 *s_ch = s_tab + A.span_w;
-  SpanCol *s_col = reinterpret_cast<SpanCol *>(s_tab + A.span_w + A.rows_per_block);
-
-  // column coefficients of the span's seams
-  for (int x = xs0 + tid; x < xs1; x += nthr) {
-    const int j = min((int)fdiv((uint32_t)x, A.div_Rw), nw - 1);
-    const int xl = x - j * A.R[2];
-    const int ew = j > 0 ? min(A.E[2], min(A.ext[2][j - 1], A.ext[2][j])) : 0;
-    if (xl < ew) s_cw[x - xs0] = coefficients_r(xl, ew, A.rcp[2][j]);
-  }
-  // row coefficients of the band's rows that lie in a row seam
-  if (A.E[1] > 0)
-    for (int k = tid; k < r1 - r0; k += nthr) {
-      const int yo = yo0 + k;
-      const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
-      const int y = yo - i * A.R[1];
-      const int eh = i > 0 ? min(A.E[1], min(A.ext[1][i - 1], A.ext[1][i])) : 0;
-      if (y < eh) s_ch[k] = coefficients_r(y, eh, A.rcp[1][i]);
+  // ---- one more round, all requested together: in lane t < jb - ja, the
+  //      extents and reciprocal of tile column j = ja + t and its pointer
+  //      pairs for the first run's tile row (and the previous chunk's); then
+  //      the frame's and the first tile row's extents and reciprocals
+  //      (scalar, pinned; the pin waits for them, so it comes last) ----
+  const bool col_lane = tid < jb - ja;
+  const int j = ja + min(tid, jb - ja - 1);
+  const uint32_t st = tau > 0 ? (uint32_t)(ptr_nh * nw) : 0u;
+  int wj = 0, wp = 0;
+  float rwj = 0.f;
+  // the pointer pairs of column j in tile row i: (i,j-1 | i,j), (i-1,j-1 |
+  // i-1,j), then the same in chunk tau-1
+  auto load_pairs = [&](int i, PtrPair (&p)[4]) {
+    const uint32_t b = ((uint32_t)(tau - taub) * (uint32_t)ptr_nh + (uint32_t)(i - ib)) * (uint32_t)nw + (uint32_t)j;
+    const uint32_t su = i > 0 ? (uint32_t)nw : 0u;
+    p[0] = pair(b);
+    p[1] = pair(b - su);
+    if (tau > 0) {
+      p[2] = pair(b - st);
+      p[3] = pair(b - st - su);
     }
-  const float2 ct = ts ? coefficients_r(f, et, A.rcp[0][tau]) : make_float2(0.f, 0.f);
-
-  const char *const *P = (const char *const *)A.ptr;
-  auto tile = [&](int tq, int ti, int tj) {
-    return P[((tq - A.taub) * A.ptr_nh + (ti - A.ib)) * nw + tj];
   };
+  PtrPair p0[4] = {}; // the first run's tile row
+  if (col_lane) {
+    wj = A.ext[2][j];
+    const int wq = A.ext[2][max(j - 1, 0)];
+    wp = j > 0 ? wq : 0;
+    rwj = A.rcp[2][j];
+    load_pairs(ia, p0);
+  }
+  const int taum = tau > 0 ? tau - 1 : 0, iam = ia > 0 ? ia - 1 : 0;
+  int tt = A.ext[0][tau], ttm = A.ext[0][taum], hia = A.ext[1][ia], hiam = A.ext[1][iam];
+  float rt = A.rcp[0][tau], rh0 = A.rcp[1][ia];
+  asm volatile("" : "+s"(tt), "+s"(ttm), "+s"(hia), "+s"(hiam), "+s"(rt), "+s"(rh0));
 
+  const int tp = tau > 0 ? ttm : 0;
+  const int et = tau > 0 ? min(E0, min(tp, tt)) : 0;
+  const bool ts = f < et;
+  const int fp = tp - et + f; // frame of chunk tau-1 blended into frame f
+  const float2 ct = ts ? coefficients_r(f, et, rt) : make_float2(0.f, 0.f);
+  // (plane, frame) slices of the chunks tau and tau-1 read here, in frames
+  const uint64_t sfm = (uint64_t)plane * (uint32_t)tt + (uint32_t)f;
+  const uint64_t sfp = (uint64_t)plane * (uint32_t)tp + (uint32_t)fp;
+
+  // The column records of tile row i, one per lane t < jb - ja, from the
+  // pairs load_pairs(i) fetched.  A record depends on the tile row, the
+  // column and the frame only (the row-seam operands are set whenever there
+  // is a tile row above; runs outside the row seam do not read them).
+  auto build_cols = [&](int i, int hi, int hp, const PtrPair (&p)[4]) {
+    const PtrPair &lm = p[0], &cu = p[1], &plm = p[2], &pcu = p[3];
+    const int eh = i > 0 ? min(E1, min(hp, hi)) : 0;
+    const int u = hp - eh;
+    const int ew = j > 0 ? min(E2, min(wp, wj)) : 0;
+    const int cw = j < nw - 1 ? R2 : wj;
+    const int l = wp - ew;
+    const uint64_t rm = sfm * (uint32_t)hi, ru = sfm * (uint32_t)hp + (uint32_t)u;
+    SpanCol C;
+    C.pitch_j = (int64_t)wj * EB;
+    C.pitch_p = (int64_t)wp * EB;
+    C.xbase = j * R2;
+    C.ews = min(ew, cw);
+    C.ew = ew;
+    C.rw = rwj;
+    C.m = (GPtr)lm.b + rm * (uint32_t)wj * EB;
+    C.u = C.l = C.c = C.pm = C.pu = C.pl = C.pc = nullptr;
+    if (i > 0) C.u = (GPtr)cu.b + ru * (uint32_t)wj * EB;
+    if (ew > 0) C.l = (GPtr)lm.a + (rm * (uint32_t)wp + (uint32_t)l) * EB;
+    if (i > 0 && ew > 0) C.c = (GPtr)cu.a + (ru * (uint32_t)wp + (uint32_t)l) * EB;
+    if (ts) {
+      const uint64_t qm = sfp * (uint32_t)hi, qu = sfp * (uint32_t)hp + (uint32_t)u;
+      C.pm = (GPtr)plm.b + qm * (uint32_t)wj * EB;
+      if (i > 0) C.pu = (GPtr)pcu.b + qu * (uint32_t)wj * EB;
+      if (ew > 0) C.pl = (GPtr)plm.a + (qm * (uint32_t)wp + (uint32_t)l) * EB;
+      if (i > 0 && ew > 0) C.pc = (GPtr)pcu.a + (qu * (uint32_t)wp + (uint32_t)l) * EB;
+    }
+    s_col[tid] = C;
+  };
+  if (col_lane) build_cols(ia, hia, hiam, p0);
+  __syncthreads();
+
+  int cur = ia, hi = hia, hp = hiam;
+  float rh = rh0;
   int yo = yo0;
   while (yo < yo1) {
-    const int i = min((int)fdiv((uint32_t)yo, A.div_Rh), nh - 1);
-    const int ybase = i * A.R[1];
-    const int hi = A.ext[1][i];
-    const int hp = i > 0 ? A.ext[1][i - 1] : 0;
-    const int eh = i > 0 ? min(A.E[1], min(hp, hi)) : 0;
-    const int chh = i < nh - 1 ? A.R[1] : hi;
+    const int i = min((int)fdiv_ms((uint32_t)yo, Rhm, Rhs), nh - 1);
+    if (i != cur) { // the band crosses into the next tile row (i > 0)
+      hp = A.ext[1][i - 1];
+      hi = A.ext[1][i];
+      rh = A.rcp[1][i];
+      cur = i;
+      PtrPair pi[4] = {};
+      if (col_lane) load_pairs(i, pi);
+      __syncthreads(); // the previous run is done with s_col
+      if (col_lane) build_cols(i, hi, hp, pi);
+      __syncthreads();
+    }
+    const int ybase = i * R1;
+    const int eh = i > 0 ? min(E1, min(hp, hi)) : 0;
+    const int chh = i < nh - 1 ? R1 : hi;
     const int ehs = min(eh, chh);
     const int yl = yo - ybase;
     const bool hs = yl < ehs;
     const int yl1 = min(hs ? ehs : chh, yl + (yo1 - yo));
-    const int u = hp - eh;
-
-    __syncthreads(); // the previous run is done with s_col (and the tables are written)
-    for (int t = tid; t < jb - ja; t += nthr) {
-      const int j = ja + t;
-      const int wj = A.ext[2][j];
-      const int wp = j > 0 ? A.ext[2][j - 1] : 0;
-      const int ew = j > 0 ? min(A.E[2], min(wp, wj)) : 0;
-      const int cw = j < nw - 1 ? A.R[2] : wj;
-      const int l = wp - ew;
-      const int64_t pj = (int64_t)wj * EB, pp = (int64_t)wp * EB;
-      SpanCol C;
-      C.pitch_j = pj;
-      C.pitch_p = pp;
-      C.xbase = j * A.R[2];
-      C.ews = min(ew, cw);
-      C.m = tile(tau, i, j) + ((plane * tt + f) * hi) * pj;
-      C.u = C.l = C.c = C.pm = C.pu = C.pl = C.pc = nullptr;
-      if (hs) C.u = tile(tau, i - 1, j) + ((plane * tt + f) * hp + u) * pj;
-      if (ew > 0) C.l = tile(tau, i, j - 1) + ((plane * tt + f) * hi) * pp + (int64_t)l * EB;
-      if (hs && ew > 0) C.c = tile(tau, i - 1, j - 1) + ((plane * tt + f) * hp + u) * pp + (int64_t)l * EB;
-      if (ts) {
-        C.pm = tile(tau - 1, i, j) + ((plane * tp + fp) * hi) * pj;
-        if (hs) C.pu = tile(tau - 1, i - 1, j) + ((plane * tp + fp) * hp + u) * pj;
-        if (ew > 0) C.pl = tile(tau - 1, i, j - 1) + ((plane * tp + fp) * hi) * pp + (int64_t)l * EB;
-        if (hs && ew > 0)
-          C.pc = tile(tau - 1, i - 1, j - 1) + ((plane * tp + fp) * hp + u) * pp + (int64_t)l * EB;
-      }
-      s_col[t] = C;
-    }
-    __syncthreads();
 
     SpanRun R;
-    R.o = (char *)A.out + (((plane * A.LT + f_out) * A.LH + ybase) * (int64_t)A.LW + xs0) * EB;
-    R.opitch = (int64_t)A.LW * EB;
+    R.o = (char *)outp + ((((uint64_t)plane * (uint32_t)LT + (uint32_t)f_out) * (uint32_t)LH + (uint32_t)ybase) *
+                              (uint32_t)LW + (uint32_t)xs0) * EB;
+    R.opitch = (int64_t)LW * EB;
     R.y0 = yl;
     R.y1 = yl1;
     R.xs0 = xs0;
     R.wv = (xs1 - xs0) / VecInfo<DT, VB>::V;
-    R.inv_wv = 1.0f / (float)R.wv;
     R.ja = ja;
     R.nw = nw;
-    R.div_Rw = A.div_Rw;
-    R.ch = s_ch + (ybase - yo0);
-    R.cw = s_cw;
+    R.Rwm = Rwm;
+    R.Rws = Rws;
+    R.eh = eh;
+    R.rh = rh;
     R.ct = ct;
     const int cls = (ts ? 2 : 0) | (hs ? 1 : 0);
     switch (cls) {

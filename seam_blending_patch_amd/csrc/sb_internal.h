@@ -34,7 +34,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
 // ---------------------------------------------------------------------------
 constexpr int kMaxAxisTiles = 64;    // tiles per axis
 constexpr int kMaxWindowTiles = 192; // tile pointers per launch window
-constexpr int kMaxBlend = 4096;      // largest clamped blend extent (LDS coefficient tables)
+constexpr int kMaxBlend = 4096;      // largest clamped blend extent (the coefficient formula is checked up to it)
 // largest grid x of the blend and ramp launches: 2^32 work-items in x at up to
 // 256 threads per block
 constexpr int64_t kMaxBlocksX = ((int64_t)1 << 24) - 1;
@@ -52,9 +52,7 @@ struct BlendArgs {
   int32_t F0, nF, Y0, nY;           // output frame / row range of this window
   int32_t plane0;                   // first (n, c) plane of this launch
   int32_t rows_per_block;           // output rows per block
-  int32_t ew_max;                   // largest column blend extent (LDS table length)
   int32_t span_k;                   // span layout: tile columns per span (0: segment layout)
-  int32_t span_w;                   // span layout: widest span in elements (LDS table length)
   int32_t off32;                    // every tile and output offset a block forms is below 2^31 bytes
   int32_t nt_store;                 // output stores with nontemporal hints (calls moving < 128 MB)
   int32_t g_seg, g_band, g_pf;      // segment kernel grid: W segments, row bands, (plane, frame) pairs
@@ -63,14 +61,21 @@ struct BlendArgs {
 
 constexpr int kMaxSpanCols = 32; // tile columns per span (span layout)
 
+// A pointer into global memory, typed so: loads through it are global loads,
+// also when the pointer itself was read from LDS or came out of an asm
+// statement (a generic pointer there would make them flat loads).
+typedef const __attribute__((address_space(1))) char *GPtr;
+
 // One tile column of a span (span layout), for one run of rows: the tiles the
 // closed form reads, each offset so that operand (y, x) of the column is at
-// base + y * pitch + x * elem_bytes; built per run in LDS.
+// base + y * pitch + x * elem_bytes, and the column seam; built per run in LDS.
 struct SpanCol {
-  const char *m, *u, *l, *c;     // tiles (i,j), (i-1,j), (i,j-1), (i-1,j-1) of chunk tau
-  const char *pm, *pu, *pl, *pc; // the same in chunk tau-1
+  GPtr m, u, l, c;               // tiles (i,j), (i-1,j), (i,j-1), (i-1,j-1) of chunk tau
+  GPtr pm, pu, pl, pc;           // the same in chunk tau-1
   int64_t pitch_j, pitch_p;      // bytes per row of tile column j and j-1
   int32_t xbase, ews;            // first output column of the column's crop; its seam width
+  int32_t ew;                    // the column seam's blend extent (0: none)
+  float rw;                      // fp32(1/ew)
 };
 
 // ---------------------------------------------------------------------------
