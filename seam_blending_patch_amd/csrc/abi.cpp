@@ -291,14 +291,24 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
       span_w = std::max(span_w, (jb == Aw.n ? Aw.L : jb * Aw.R) - ja * Aw.R);
     }
   }
+  // The span layout's launches are small (the tiled-encode latents, a few MB):
+  // its blocks are sized so that the grid is about one round of resident
+  // blocks (SB_BLEND_SPAN_BLOCKS_PER_CU per CU at the kernel's occupancy),
+  // with at least SB_BLEND_SPAN_PER_BLOCK_MIN vectors each.  Measured against
+  // the segment layout's 18 per CU and a 512-vector minimum: SD encode 2048
+  // 4.95 -> 4.62 us, 64/32 encode 5.37 -> 4.59 us, the batch-4 4096 encode and
+  // the 112x112 fp32 blend unchanged.
+#ifndef SB_BLEND_SPAN_BLOCKS_PER_CU
+#define SB_BLEND_SPAN_BLOCKS_PER_CU 4
+#endif
 #ifndef SB_BLEND_SPAN_PER_BLOCK_MIN
-#define SB_BLEND_SPAN_PER_BLOCK_MIN 512
+#define SB_BLEND_SPAN_PER_BLOCK_MIN 128
 #endif
   const int64_t block_cols = span ? span_w / V : seg_max;
   const int64_t per_block_l = span ? std::min<int64_t>(
                                          SB_BLEND_PER_BLOCK_MAX,
                                          std::max<int64_t>(SB_BLEND_SPAN_PER_BLOCK_MIN,
-                                                           total_vec / ((int64_t)cus * SB_BLEND_BLOCKS_PER_CU)))
+                                                           total_vec / ((int64_t)cus * SB_BLEND_SPAN_BLOCKS_PER_CU)))
                                    : per_block;
   int64_t rows_pb = std::max<int64_t>(1, std::min<int64_t>(1024, per_block_l / block_cols));
   rows_pb = std::min<int64_t>(rows_pb, Ah.L);
@@ -307,8 +317,9 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   // g = gcd(R_h, e_h(1), ..., e_h(n-1)) rows from a tile row's origin, so a
   // band height dividing g keeps them all on band edges.  Taken when a divisor
   // of g comes within a factor of 3 of the size-based height (measured on the
-  // video workload: 64-row bands 68.6 us against 69.7 us for 60-row ones);
-  // otherwise the bands are balanced over the rows.
+  // video workload: 64-row bands 68.6 us against 69.7 us for 60-row ones; in
+  // the span layout a band that crosses a tile row also rebuilds its column
+  // records); otherwise the bands are balanced over the rows.
   int64_t g = Ah.R;
   for (int64_t k = 1; k < Ah.n; ++k)
     if (Ah.e[k] > 0) g = std::gcd(g, Ah.e[k]);
@@ -318,7 +329,7 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
       if (d <= rows_pb) aligned_rows = std::max(aligned_rows, d);
       if (g / d <= rows_pb) aligned_rows = std::max(aligned_rows, g / d);
     }
-  if (!span && Ah.n > 1 && aligned_rows * 3 >= rows_pb) {
+  if (Ah.n > 1 && aligned_rows * 3 >= rows_pb) {
     rows_pb = aligned_rows;
   } else {
     const int64_t nrb = (Ah.L + rows_pb - 1) / rows_pb;
