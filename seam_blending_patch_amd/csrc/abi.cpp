@@ -427,7 +427,7 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
 // --------------------------------------------------------------------------
 namespace {
 
-// largest pass-1 grid: blocks of 256 threads (1024 for the whole-row
+// largest pass-1 grid: blocks of 512 threads (1024 for the whole-row
 // layout) within 2^32 work-items in x
 constexpr int64_t kMaxStatsBlocks = ((int64_t)1 << 32) / 1024 - 1;
 
@@ -505,7 +505,7 @@ int plan_groupnorm(int ndim, const int64_t *shape, int64_t groups, int split_axi
 #ifndef SB_GN_CHUNK_MIN
 #define SB_GN_CHUNK_MIN 8192
 #endif
-  // pass 1 launches at most kMaxStatsBlocks blocks (2^32 work-items of 256
+  // pass 1 launches at most kMaxStatsBlocks blocks (2^32 work-items of 1024
   // threads in x): more chunks only while the grid stays within that
   // (counted for the per-patch layout, which has the most blocks, so that the
   // chunk count and the workspace do not depend on the vector width)
