@@ -59,6 +59,8 @@
 #ifndef SB_BLEND_THREADS
 #define SB_BLEND_THREADS 256
 #endif
+// the host puts up to kMaxBlocksX blocks on grid x of a span launch
+static_assert(sb::kMaxBlocksX * SB_BLEND_THREADS < ((int64_t)1 << 32), "grid x within 2^32 work-items");
 #ifndef SB_BLEND_LOADS
 #define SB_BLEND_LOADS 8 // 16-byte loads per lane in flight per batch
 #endif
@@ -571,8 +573,11 @@ __global__ __launch_bounds__(SB_BLEND_THREADS) SB_BLEND_OCC void blend_stitch_ke
 // rows.  Here a block owns a span of whole tile columns instead and walks its
 // rows left to right, so consecutive lanes read consecutive vectors; the
 // column class (seam or body) and the tile column vary per lane, the row and
-// frame classes stay block-uniform per run.  Same closed form, same
-// arithmetic, element by element through fp32.
+// frame classes stay block-uniform per run.  Same closed form and the same
+// roundings (16-bit types in packed pairs, as in run_rows); the column records
+// of a tile row (tile bases, seam extent and reciprocal) are built once per
+// tile row in LDS, one lane per column, and the seam coefficients are formed
+// in registers.
 // ---------------------------------------------------------------------------
 #ifndef SB_SPAN_U
 #define SB_SPAN_U 2

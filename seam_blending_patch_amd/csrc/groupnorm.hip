@@ -211,6 +211,8 @@ __device__ __forceinline__ void accumulate_batch(Stat &st, const Vec<VB> (&v)[kS
 }
 
 constexpr int kStatsThreads = 64 * kStatsWaves; // threads per pass-1 block (a constant: no launch-argument read)
+// the host caps pass-1 grids counting blocks of up to 1024 threads
+static_assert(kStatsThreads <= 1024, "pass-1 blocks of at most 1024 threads");
 
 template <int DT, int VB>
 __global__ __launch_bounds__(kStatsThreads) void gn_stats_kernel(const GNArgs A, FastDiv div_big,

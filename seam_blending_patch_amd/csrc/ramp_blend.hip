@@ -27,6 +27,8 @@
 #ifndef SB_RAMP_THREADS
 #define SB_RAMP_THREADS 256
 #endif
+// the host puts up to kMaxBlocksX planes on grid x of a launch
+static_assert(sb::kMaxBlocksX * SB_RAMP_THREADS < ((int64_t)1 << 32), "grid x within 2^32 work-items");
 #ifndef SB_RAMP_BATCH
 #define SB_RAMP_BATCH 1 // items whose loads are issued together (more costs occupancy; measured best)
 #endif
