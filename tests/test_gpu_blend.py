@@ -93,6 +93,20 @@ def test_random_grids_scalar_path(sb, dtype, ndim):
         check(sb, w, workloads.draw_tiles(w), "random-scalar")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("ndim", [4, 5])
+def test_random_narrow_seam_grids(sb, dtype, ndim):
+    # Small vector-aligned extents and row limits, so nearly every W segment is
+    # under 16 vectors and the narrow-seam (span) layout runs: many tile
+    # columns per span, row bands that cross tile rows and row seams, frame
+    # seams in 5-D, and 16-bit types in packed pairs.
+    align = 4 if dtype == "fp32" else 8
+    for seed in range(40):
+        w = workloads.random_blend_workload(5000 + seed, dtype, ndim=ndim, max_tiles=6, max_ext=64,
+                                            align=align, N=2, C=3)
+        check(sb, w, workloads.draw_tiles(w), "random-narrow")
+
+
 def _wl(dtype, ext_h, ext_w, E, R, ndim=4, ext_t=(1,), Et=0, Rt=1, N=1, C=3, seed=7):
     return workloads.BlendWorkload("edge", dtype, ndim, N, C, list(ext_t), list(ext_h), list(ext_w),
                                    (Et, E, E), (Rt, R, R), seed=seed)
