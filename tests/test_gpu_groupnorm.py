@@ -109,6 +109,35 @@ def test_random_shapes(sb, dtype):
         check(sb, gw, x, g, b, f"case {k}")
 
 
+def _random_case(rng):
+    # a random activation: 3-D to 5-D, 1-32 groups of 1-8 channels, split
+    # along any spatial axis into 1 to a few more patches than positions
+    ndim = int(rng.integers(3, 6))
+    N = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    C = G * int(rng.choice([1, 2, 3, 4, 8]))
+    hi = {3: 400, 4: 64, 5: 24}[ndim]
+    spatial = [int(rng.integers(1, hi + 1)) for _ in range(ndim - 2)]
+    axis = int(rng.integers(2, ndim))
+    L = spatial[axis - 2]
+    P = int(rng.integers(1, min(64, L + 2) + 1))
+    return (N, C, *spatial), G, axis, P
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_random_activations_many_seeds(sb, dtype):
+    # 60 random shapes per dtype: every patch layout the host can pick (patch
+    # runs, whole-row blocks, empty patches), vector and scalar paths, with and
+    # without affine and per-patch offsets; fp32 at the 1e-5 reading
+    rng = np.random.default_rng(77 if dtype == "fp32" else 78)
+    for k in range(60):
+        shape, G, axis, P = _random_case(rng)
+        offset = ("uniform", -2.0, 2.0) if k % 2 == 0 else None
+        gw = _gw(shape, dtype, G, axis, P, seed=700 + k, affine=(k % 3 != 1), offset=offset)
+        x, g, b = workloads.draw_groupnorm(gw)
+        check(sb, gw, x, g, b, f"random {k}")
+
+
 def test_constant_group_gives_beta_exactly(sb):
     gw = _gw((1, 16, 8, 8), "fp32", 4, 2, 2, seed=1, offset=None)
     x = np.full(gw.shape, 2.5, np.float32)
