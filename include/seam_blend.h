@@ -98,9 +98,13 @@ int vae_tile_blend_stitch_output_extents(const int64_t grid[6], const int64_t *t
  * Each output element is written exactly once; no scratch memory.
  * N*C == 0 is a no-op that accepts null tile and output pointers.
  * Limits (SB_EGEOM beyond them, before any launch): clamped blend extents up
- * to 4096; when every W seam and crop is narrower than 16 vectors (the
- * narrow-seam layout) a launch window of more than 2^24 - 1 output frames is
- * refused; otherwise any frame count is taken, in several launches.
+ * to 4096; a launch window takes at most 192 tile pointers, a window's tile
+ * rows with the row above and its temporal tiles with the one before, so up
+ * to 48 tile columns always fit and more may be refused when there are several
+ * tile rows or temporal tiles; when every W seam and crop is narrower than 16
+ * vectors (the narrow-seam layout) a launch window of more than 2^24 - 1
+ * output frames is refused; otherwise any frame count is taken, in several
+ * launches.
  */
 int vae_tile_blend_stitch(const void *const *tiles, const int64_t grid[6],
                           const int64_t *tile_extents, const int64_t blend_extent[3],
@@ -116,9 +120,9 @@ size_t patch_groupnorm_workspace_bytes(int ndim, const int64_t *shape, int64_t g
 /*
  * GroupNorm of x viewed as n_patches patches along split_axis.
  *   x            device pointer, contiguous [N, C, spatial...] of dtype, ndim 3..5.
- *   shape        host array of ndim extents; C % groups == 0; N*C < 2^31 and
- *                each group (C/G * spatial elements) < 2^31 elements (else
- *                SB_EGEOM).
+ *   shape        host array of ndim extents; C % groups == 0; N*C < 2^31,
+ *                each group (C/G * spatial elements) < 2^31 elements and the
+ *                tensor < 2^56 bytes (else SB_EGEOM).
  *   split_axis   2 <= split_axis < ndim: the spatial axis the patches cut.
  *   n_patches    1..64.  Patch p covers [s_p, s_p + len_p) along split_axis
  *                with the first (L mod P) patches one longer (empty patches

@@ -350,74 +350,88 @@ extern "C" int vae_tile_blend_stitch(const void *const *tiles, const int64_t gri
   // [t0, t1) and rows of tile rows [i0, i1); it needs the tile pointers of
   // temporal tiles [max(t0-1,0), t1) and tile rows [max(i0-1,0), i1).
   // Windows are grown greedily within the kernel-argument pointer budget.
+  // Every window is planned and checked before the first launch, so a
+  // geometry error leaves the output untouched.
   auto tiles_needed = [&](int64_t t0, int64_t t1, int64_t i0, int64_t i1) {
     return (t1 - std::max<int64_t>(t0 - 1, 0)) * (i1 - std::max<int64_t>(i0 - 1, 0)) * Aw.n;
   };
-  int64_t t0 = 0;
-  while (t0 < At.n) {
+  struct Window {
+    int64_t t0, t1, i0, i1;
+  };
+  std::vector<Window> wins;
+  for (int64_t t0 = 0; t0 < At.n;) {
     int64_t t1 = t0 + 1;
     while (t1 < At.n && tiles_needed(t0, t1 + 1, 0, Ah.n) <= sb::kMaxWindowTiles) ++t1;
-    int64_t i0 = 0;
-    while (i0 < Ah.n) {
+    for (int64_t i0 = 0; i0 < Ah.n;) {
       int64_t i1 = i0 + 1;
       if (tiles_needed(t0, t1, i0, i1) > sb::kMaxWindowTiles)
         return fail(SB_EGEOM, "tile grid too wide: %lld tiles per row exceed one launch window",
                     (long long)Aw.n);
       while (i1 < Ah.n && tiles_needed(t0, t1, i0, i1 + 1) <= sb::kMaxWindowTiles) ++i1;
-      const int64_t tb = std::max<int64_t>(t0 - 1, 0), ib = std::max<int64_t>(i0 - 1, 0);
-      A.taub = (int32_t)tb;
-      A.ib = (int32_t)ib;
-      A.ptr_nh = (int32_t)(i1 - ib);
-      for (int k = 0; k < sb::kMaxWindowTiles; ++k) A.ptr[k] = nullptr;
-      for (int64_t tq = tb; tq < t1; ++tq)
-        for (int64_t iq = ib; iq < i1; ++iq)
-          for (int64_t jq = 0; jq < Aw.n; ++jq)
-            A.ptr[((tq - tb) * A.ptr_nh + (iq - ib)) * Aw.n + jq] = tiles[(tq * Ah.n + iq) * Aw.n + jq];
-      const int64_t F0 = t0 * At.R, F1 = (t1 == At.n) ? At.L : t1 * At.R;
-      const int64_t Y0 = i0 * Ah.R, Y1 = (i1 == Ah.n) ? Ah.L : i1 * Ah.R;
-      A.F0 = (int32_t)F0; A.nF = (int32_t)(F1 - F0);
-      A.Y0 = (int32_t)Y0; A.nY = (int32_t)(Y1 - Y0);
-      const int64_t row_blocks = (A.nY + rows_pb - 1) / rows_pb;
       if (span) {
-        // span kernel: grid x = (plane, frame) pairs of this window, y = spans,
-        // z = row bands; x stays within 2^32 work-items (kMaxBlocksX blocks)
-        A.div_nF = sb::make_fastdiv((uint32_t)A.nF);
-        if (A.nF > sb::kMaxBlocksX)
-          return fail(SB_EGEOM, "a launch window of %d frames exceeds %lld blocks", A.nF,
+        // the span kernel's grid x takes the window's (plane, frame) pairs:
+        // at least its frames, within 2^32 work-items (kMaxBlocksX blocks)
+        const int64_t nF = ((t1 == At.n) ? At.L : t1 * At.R) - t0 * At.R;
+        if (nF > sb::kMaxBlocksX)
+          return fail(SB_EGEOM, "a launch window of %lld frames exceeds %lld blocks", (long long)nF,
                       (long long)sb::kMaxBlocksX);
-        const int64_t max_planes = std::max<int64_t>(1, sb::kMaxBlocksX / A.nF);
-        for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
-          const int64_t np = std::min(max_planes, planes - p0);
-          A.plane0 = (int32_t)p0;
-          const dim3 grid((unsigned)(np * A.nF), (unsigned)n_wseg, (unsigned)row_blocks);
-          hipError_t e = sb_launch_blend_span(A, dtype, vec16 ? 1 : 0, grid, lds, st);
-          if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
-        }
-      } else {
-        // segment kernel: grid (W segments, row bands, (plane, frame) pairs),
-        // at most kMaxBlocksYZ pairs per launch: the window's frames go in
-        // ranges of at most that many, and planes as many as fit beside them
-        for (int64_t fa = F0; fa < F1; fa += sb::kMaxBlocksYZ) {
-          const int64_t nf = std::min<int64_t>(sb::kMaxBlocksYZ, F1 - fa);
-          A.F0 = (int32_t)fa;
-          A.nF = (int32_t)nf;
-          A.div_nF = sb::make_fastdiv((uint32_t)nf);
-          const int64_t max_planes = std::max<int64_t>(1, sb::kMaxBlocksYZ / nf);
-          for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
-            const int64_t np = std::min(max_planes, planes - p0);
-            A.plane0 = (int32_t)p0;
-            A.g_seg = (int32_t)n_wseg;
-            A.g_band = (int32_t)row_blocks;
-            A.g_pf = (int32_t)(np * nf);
-            const dim3 grid((unsigned)n_wseg, (unsigned)row_blocks, (unsigned)(np * nf));
-            hipError_t e = sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid, lds, st);
-            if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
-          }
-        }
       }
+      wins.push_back(Window{t0, t1, i0, i1});
       i0 = i1;
     }
     t0 = t1;
+  }
+
+  for (const Window &w : wins) {
+    const int64_t t0 = w.t0, t1 = w.t1, i0 = w.i0, i1 = w.i1;
+    const int64_t tb = std::max<int64_t>(t0 - 1, 0), ib = std::max<int64_t>(i0 - 1, 0);
+    A.taub = (int32_t)tb;
+    A.ib = (int32_t)ib;
+    A.ptr_nh = (int32_t)(i1 - ib);
+    for (int k = 0; k < sb::kMaxWindowTiles; ++k) A.ptr[k] = nullptr;
+    for (int64_t tq = tb; tq < t1; ++tq)
+      for (int64_t iq = ib; iq < i1; ++iq)
+        for (int64_t jq = 0; jq < Aw.n; ++jq)
+          A.ptr[((tq - tb) * A.ptr_nh + (iq - ib)) * Aw.n + jq] = tiles[(tq * Ah.n + iq) * Aw.n + jq];
+    const int64_t F0 = t0 * At.R, F1 = (t1 == At.n) ? At.L : t1 * At.R;
+    const int64_t Y0 = i0 * Ah.R, Y1 = (i1 == Ah.n) ? Ah.L : i1 * Ah.R;
+    A.F0 = (int32_t)F0; A.nF = (int32_t)(F1 - F0);
+    A.Y0 = (int32_t)Y0; A.nY = (int32_t)(Y1 - Y0);
+    const int64_t row_blocks = (A.nY + rows_pb - 1) / rows_pb;
+    if (span) {
+      // span kernel: grid x = (plane, frame) pairs of this window, y = spans,
+      // z = row bands
+      A.div_nF = sb::make_fastdiv((uint32_t)A.nF);
+      const int64_t max_planes = std::max<int64_t>(1, sb::kMaxBlocksX / A.nF);
+      for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
+        const int64_t np = std::min(max_planes, planes - p0);
+        A.plane0 = (int32_t)p0;
+        const dim3 grid((unsigned)(np * A.nF), (unsigned)n_wseg, (unsigned)row_blocks);
+        hipError_t e = sb_launch_blend_span(A, dtype, vec16 ? 1 : 0, grid, lds, st);
+        if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
+      }
+    } else {
+      // segment kernel: grid (W segments, row bands, (plane, frame) pairs),
+      // at most kMaxBlocksYZ pairs per launch: the window's frames go in
+      // ranges of at most that many, and planes as many as fit beside them
+      for (int64_t fa = F0; fa < F1; fa += sb::kMaxBlocksYZ) {
+        const int64_t nf = std::min<int64_t>(sb::kMaxBlocksYZ, F1 - fa);
+        A.F0 = (int32_t)fa;
+        A.nF = (int32_t)nf;
+        A.div_nF = sb::make_fastdiv((uint32_t)nf);
+        const int64_t max_planes = std::max<int64_t>(1, sb::kMaxBlocksYZ / nf);
+        for (int64_t p0 = 0; p0 < planes; p0 += max_planes) {
+          const int64_t np = std::min(max_planes, planes - p0);
+          A.plane0 = (int32_t)p0;
+          A.g_seg = (int32_t)n_wseg;
+          A.g_band = (int32_t)row_blocks;
+          A.g_pf = (int32_t)(np * nf);
+          const dim3 grid((unsigned)n_wseg, (unsigned)row_blocks, (unsigned)(np * nf));
+          hipError_t e = sb_launch_blend(A, dtype, vec16 ? 1 : 0, grid, lds, st);
+          if (e != hipSuccess) return fail(SB_ELAUNCH, "blend launch failed: %s", hipGetErrorString(e));
+        }
+      }
+    }
   }
   return SB_OK;
 }
@@ -575,9 +589,13 @@ int groupnorm_call(const void *x, int ndim, const int64_t *shape, int64_t groups
   const int EB = elem_bytes(dtype);
   if (!aligned(x, EB) || !aligned(out, EB) || (gamma && !aligned(gamma, EB)) || (beta && !aligned(beta, EB)))
     return fail(SB_EARG, "x, out, gamma and beta must be aligned to the element size");
+  // N*C < 2^31 and a group below 2^31 elements, so a plane holds fewer than
+  // 2^31 elements and the tensor fewer than 2^62
+  const uint64_t nbytes = (uint64_t)(shape[0] * shape[1] * P.a.S) * (uint64_t)EB;
+  if (nbytes >= ((uint64_t)1 << 56)) return fail(SB_EGEOM, "tensor too large (2^56 bytes or more)");
   if (x != out) {
-    const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)(shape[0] * shape[1] * P.a.S * EB);
-    const uintptr_t y0 = (uintptr_t)out, y1 = y0 + (uintptr_t)(shape[0] * shape[1] * P.a.S * EB);
+    const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)nbytes;
+    const uintptr_t y0 = (uintptr_t)out, y1 = y0 + (uintptr_t)nbytes;
     if (x0 < y1 && y0 < x1) return fail(SB_EARG, "out partially overlaps x (only exact aliasing is allowed)");
   }
   bool vec16 = P.vec16 && aligned(x, 16) && aligned(out, 16);

@@ -208,6 +208,25 @@ def test_sizes_beyond_the_index_range_are_rejected_on_host(sb):
     assert b"frames exceeds" in lib.seamblend_last_error()
 
 
+def test_too_wide_tile_grid_is_refused_before_any_launch(sb):
+    # 64 tile columns, 2 tile rows, 2 temporal tiles: the first launch windows
+    # fit the 192-entry pointer table, the window of tile row 1 in temporal
+    # tile 1 (with the row above and the chunk before: 4 x 64 pointers) does
+    # not.  Every window is planned first, so the call fails with a geometry
+    # error before it launches anything (a launch here, with no GPU, would
+    # report a launch error instead).
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    lib.vae_tile_blend_stitch.restype = ctypes.c_int
+    lib.seamblend_last_error.restype = ctypes.c_char_p
+    i64 = lambda v: (ctypes.c_int64 * len(v))(*v)  # noqa: E731
+    n = 2 * 2 * 64
+    fake = (ctypes.c_void_p * n)(*[(k + 1) << 16 for k in range(n)])
+    rc = lib.vae_tile_blend_stitch(fake, i64([5, 1, 1, 2, 2, 64]), i64([4, 4, 8, 8] + [8] * 64),
+                                   i64([0, 0, 0]), i64([4, 8, 8]), 0, ctypes.c_void_p(1 << 40), None)
+    assert rc == -2
+    assert b"too wide" in lib.seamblend_last_error()
+
+
 def test_row_limit_and_blend_extent_beyond_32_bits(sb):
     # a row limit above 2^30 is rejected (it would not fit the kernel's 32-bit
     # index arithmetic); a huge blend extent is the same as one clamped to the
