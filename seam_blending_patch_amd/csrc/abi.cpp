@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <numeric>
 #include <cstdarg>
 #include <cstdio>
@@ -108,16 +109,18 @@ int build_grid(const int64_t grid[6], const int64_t *tile_extents, const int64_t
 // device properties cached per device (no allocation)
 // --------------------------------------------------------------------------
 int cu_count() {
-  static int cached[64] = {0};
+  // calls may come from several host threads: each entry is written once,
+  // always with the same value
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
