@@ -192,12 +192,14 @@ def summarize_trace(trace_dir, title, command):
     return "\n".join(lines) + "\n"
 
 
-def pmc_command(what):
-    """The commands that make one profile mode's traffic records."""
-    return (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_FETCH_SIZE_{what} -o run -- "
+def pmc_command(what, fetch_dir=None, write_dir=None):
+    """The commands that make one profile mode's traffic records, with the
+    counter runs' output directories as given (placeholders when none)."""
+    fetch_dir = fetch_dir or f"<out>/pmc_FETCH_SIZE_{what}"
+    write_dir = write_dir or f"<out>/pmc_WRITE_SIZE_{what}"
+    return (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- "
             f"python3 bench.py --profile {what} --steps 3 --warmup 1; the same with WRITE_SIZE into "
-            f"gpurun_out/pmc_WRITE_SIZE_{what}; python3 -m benchkit.traffic traffic {what} "
-            f"gpurun_out/pmc_FETCH_SIZE_{what} gpurun_out/pmc_WRITE_SIZE_{what}")
+            f"{write_dir}; python3 -m benchkit.traffic traffic {what} {fetch_dir} {write_dir}")
 
 
 def traffic_table(path=None):
@@ -221,7 +223,7 @@ def traffic_table(path=None):
 
 def main(argv):
     if len(argv) >= 4 and argv[0] == "traffic":
-        write_traffic(argv[2], argv[3], argv[1], command=pmc_command(argv[1]))
+        write_traffic(argv[2], argv[3], argv[1], command=pmc_command(argv[1], argv[2], argv[3]))
     elif len(argv) >= 2 and argv[0] == "table":
         md = traffic_table()
         with open(argv[1], "w") as f:
